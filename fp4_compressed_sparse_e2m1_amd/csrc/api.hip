@@ -1,0 +1,374 @@
+// C ABI of libcsa2: argument validation, workspace planning and launches.
+// The operations and their sources are documented in include/csa2.h.
+#include <math.h>
+
+#include <mutex>
+
+#include "../../include/csa2.h"
+#include "internal.h"
+
+using namespace csa2;
+
+namespace {
+
+constexpr int kMaxBlocks = 4096;
+constexpr int kMaxPos = 4096;
+constexpr int kMaxAttnPos = 65536;
+constexpr int kMaxGridY = 65535;
+constexpr size_t kAlign = 256;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Levels of the chunked Top-k selection for rows of up to n_max keys.
+int plan_levels(int64_t n_max, int k, int64_t *chunks) {
+  int levels = 0;
+  int64_t n = n_max;
+  while (n > kSelectChunk && levels < 7) {
+    const int64_t ch = (n + kSelectChunk - 1) / kSelectChunk;
+    chunks[levels++] = ch;
+    n = ch * k;
+  }
+  chunks[levels++] = 1;
+  return levels;
+}
+
+// Bytes of one ping-pong buffer (keys + ids) of a selection.
+size_t select_scratch(int32_t rows, int64_t n_max, int k) {
+  int64_t chunks[8];
+  const int levels = plan_levels(n_max, k, chunks);
+  if (levels == 1) return 0;
+  return (size_t)rows * (size_t)chunks[0] * (size_t)k * 8;
+}
+
+struct Layout {
+  size_t keys_a = 0;    // block keys or flat entry keys
+  size_t keys_b = 0;    // pool candidate keys
+  size_t ping = 0, pong = 0;
+  size_t half = 0;      // bytes of one ping-pong buffer
+  size_t total = 0;
+};
+
+// Workspace layout of an indexer call.
+Layout plan_workspace(int32_t op, int32_t rows, int32_t max_nvis, int32_t k_blocks, int32_t k_pos) {
+  Layout L;
+  size_t off = 0;
+  size_t half = 0;
+  if (k_blocks > 0) {
+    if (op == CSA2_OP_INDEX_FULL) {
+      const int64_t nb = ((int64_t)max_nvis + 7) / 8;
+      L.keys_a = off;
+      off += round_up((size_t)rows * (size_t)(nb > 0 ? nb : 1) * 4);
+      half = select_scratch(rows, nb, k_blocks);
+    }
+    L.keys_b = off;
+    off += round_up((size_t)rows * (size_t)k_blocks * 8 * 4);
+    const size_t h2 = select_scratch(rows, (int64_t)k_blocks * 8, k_pos);
+    half = half > h2 ? half : h2;
+  } else {
+    L.keys_a = off;
+    off += round_up((size_t)rows * (size_t)(max_nvis > 0 ? max_nvis : 1) * 4);
+    half = select_scratch(rows, max_nvis, k_pos);
+  }
+  half = round_up(half);
+  L.half = half;
+  L.ping = off;
+  off += half;
+  L.pong = off;
+  off += half;
+  L.total = off;
+  return L;
+}
+
+std::once_flag g_prepare_once;
+hipError_t g_prepare_status = hipSuccess;
+
+hipError_t prepare() {
+  std::call_once(g_prepare_once, [] {
+    g_prepare_status = prepare_select();
+    if (g_prepare_status == hipSuccess) g_prepare_status = prepare_attention();
+  });
+  return g_prepare_status;
+}
+
+struct SelectOut {
+  int32_t *out;
+  int32_t *n_out;
+  int32_t map_kind;
+  const int32_t *pool_blocks;
+  const int32_t *n_pool;
+  int32_t k_blocks;
+};
+
+hipError_t run_select(const uint32_t *keys, int64_t stride, int count_kind, int count_fixed,
+                      int64_t n_max, int k, const int32_t *row_seq, const int32_t *row_nvis,
+                      int32_t n_seq, int32_t max_nvis, const SelectOut &fin, uint8_t *ping,
+                      uint8_t *pong, size_t half, int32_t rows, hipStream_t stream) {
+  int64_t chunks[8];
+  const int levels = plan_levels(n_max, k, chunks);
+  const uint32_t *kin = keys;
+  const int32_t *iin = nullptr;
+  int64_t in_stride = stride;
+  int ckind = count_kind;
+  int cfixed = count_fixed;
+  for (int l = 0; l < levels; ++l) {
+    SelectArgs a = {};
+    a.keys_in = kin;
+    a.ids_in = iin;
+    a.in_stride = in_stride;
+    a.count_kind = ckind;
+    a.count_fixed = cfixed;
+    a.row_seq = row_seq;
+    a.row_nvis = row_nvis;
+    a.n_seq = n_seq;
+    a.max_nvis = max_nvis;
+    a.k = k;
+    const bool final_level = (l == levels - 1);
+    if (!final_level) {
+      uint8_t *buf = (l % 2 == 0) ? ping : pong;
+      const int64_t out_stride = chunks[l] * k;
+      a.keys_out = reinterpret_cast<uint32_t *>(buf);
+      a.ids_out = reinterpret_cast<int32_t *>(buf + half / 2);
+      a.out_stride = out_stride;
+      hipError_t e = launch_select(a, rows, (int32_t)chunks[l], false, stream);
+      if (e != hipSuccess) return e;
+      kin = a.keys_out;
+      iin = a.ids_out;
+      in_stride = out_stride;
+      ckind = kCountFixed;
+      cfixed = (int)out_stride;
+    } else {
+      a.out = fin.out;
+      a.n_out = fin.n_out;
+      a.map_kind = fin.map_kind;
+      a.pool_blocks = fin.pool_blocks;
+      a.n_pool = fin.n_pool;
+      a.k_blocks = fin.k_blocks;
+      hipError_t e = launch_select(a, rows, 1, true, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+bool cache_ok(const csa2_cache *c, bool need_kv, bool need_ik) {
+  if (!c || c->cap < 1 || c->n_seq < 1) return false;
+  if (need_kv && (!c->kv_codes || !c->kv_scales || !aligned(c->kv_codes, 16) ||
+                  !aligned(c->kv_scales, 2)))
+    return false;
+  if (need_ik && (!c->ik_codes || !c->ik_scales || !aligned(c->ik_codes, 16))) return false;
+  return true;
+}
+
+// Shared body of index_full / index_reindex.
+csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                        const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                        int32_t max_nvis, const int32_t *pool_in, const int32_t *n_pool_in,
+                        int32_t k_blocks, int32_t k_pos, int32_t *pool_out, int32_t *n_pool_out,
+                        int32_t *topk, int32_t *n_topk, void *workspace, size_t workspace_bytes,
+                        void *stream_ptr) {
+  if (!cache_ok(cache, false, true)) return CSA2_E_INVALID_ARG;
+  if (!q_idx || !w || !row_seq || !row_nvis || !topk || !n_topk) return CSA2_E_INVALID_ARG;
+  if (n_rows < 1 || max_nvis < 0 || (int64_t)max_nvis > cache->cap || k_pos < 1 || k_blocks < 0)
+    return CSA2_E_INVALID_ARG;
+  if (!aligned(q_idx, 16) || !aligned(w, 4)) return CSA2_E_INVALID_ARG;
+  if (n_rows > kMaxGridY || k_pos > kMaxPos || k_blocks > kMaxBlocks ||
+      max_nvis > 0x7FFFFFF0)
+    return CSA2_E_UNSUPPORTED;
+  const bool pool_mode = k_blocks > 0;
+  if (op == CSA2_OP_INDEX_FULL && pool_mode && (!pool_out || !n_pool_out)) return CSA2_E_INVALID_ARG;
+  if (op == CSA2_OP_INDEX_REINDEX && pool_mode && (!pool_in || !n_pool_in)) return CSA2_E_INVALID_ARG;
+  const Layout L = plan_workspace(op, n_rows, max_nvis, k_blocks, k_pos);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
+  if (prepare() != hipSuccess) return CSA2_E_HIP;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  ScoreArgs sa = {};
+  sa.ik_codes = cache->ik_codes;
+  sa.ik_scales = cache->ik_scales;
+  sa.cap = cache->cap;
+  sa.n_seq = cache->n_seq;
+  sa.q_idx = q_idx;
+  sa.w = w;
+  sa.row_seq = row_seq;
+  sa.row_nvis = row_nvis;
+  sa.max_nvis = max_nvis;
+  hipError_t e = hipSuccess;
+
+  if (!pool_mode) {
+    // flat: every visible entry is a candidate
+    sa.keys_out = reinterpret_cast<uint32_t *>(ws + L.keys_a);
+    sa.out_stride = max_nvis > 0 ? max_nvis : 1;
+    e = launch_score(kScoreFlat, sa, n_rows, max_nvis, stream);
+    if (e != hipSuccess) return CSA2_E_HIP;
+    SelectOut fin = {topk, n_topk, kMapId, nullptr, nullptr, 0};
+    e = run_select(sa.keys_out, sa.out_stride, kCountNvis, 0, max_nvis, k_pos, row_seq, row_nvis,
+                   cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half, n_rows, stream);
+    return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+  }
+
+  const int32_t *pool = pool_in;
+  const int32_t *npool = n_pool_in;
+  if (op == CSA2_OP_INDEX_FULL) {
+    // scan: block max of every visible entry's score, then the block Top-k
+    const int64_t nb = ((int64_t)max_nvis + 7) / 8;
+    sa.keys_out = reinterpret_cast<uint32_t *>(ws + L.keys_a);
+    sa.out_stride = nb > 0 ? nb : 1;
+    e = launch_score(kScoreBlockMax, sa, n_rows, max_nvis, stream);
+    if (e != hipSuccess) return CSA2_E_HIP;
+    SelectOut fin = {pool_out, n_pool_out, kMapId, nullptr, nullptr, 0};
+    e = run_select(sa.keys_out, sa.out_stride, kCountNvisBlocks, 0, nb, k_blocks, row_seq, row_nvis,
+                   cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half, n_rows, stream);
+    if (e != hipSuccess) return CSA2_E_HIP;
+    pool = pool_out;
+    npool = n_pool_out;
+  }
+  // re-score the pool's entries and keep the best k_pos positions
+  sa.pool_blocks = pool;
+  sa.n_pool = npool;
+  sa.k_blocks = k_blocks;
+  sa.keys_out = reinterpret_cast<uint32_t *>(ws + L.keys_b);
+  sa.out_stride = (int64_t)k_blocks * 8;
+  e = launch_score(kScorePool, sa, n_rows, (int64_t)k_blocks * 8, stream);
+  if (e != hipSuccess) return CSA2_E_HIP;
+  SelectOut fin = {topk, n_topk, kMapPool, pool, npool, k_blocks};
+  e = run_select(sa.keys_out, sa.out_stride, kCountFixed, k_blocks * 8, (int64_t)k_blocks * 8, k_pos,
+                 row_seq, row_nvis, cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half,
+                 n_rows, stream);
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
+bool swa_ok(const csa2_swa *s) {
+  return s && s->kv && s->row_end && s->len >= 0 && s->window >= 0 && s->window <= 1024 &&
+         aligned(s->kv, 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t group,
+                              const int64_t *dst_rows, uint8_t *codes, uint8_t *scales,
+                              void *stream) {
+  if (n < 0) return CSA2_E_INVALID_ARG;
+  if (group != 16 && group != 32) return CSA2_E_UNSUPPORTED;
+  if (dim < 32 || dim > 4096 || dim % group != 0) return CSA2_E_UNSUPPORTED;
+  if (n == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_E_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, group == 16 ? 8 : 16)) return CSA2_E_INVALID_ARG;
+  if (n > ((int64_t)1 << 40) / dim) return CSA2_E_UNSUPPORTED;
+  hipError_t e = launch_quantize(x, n, dim, group, dst_rows, codes, scales,
+                                 reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
+size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,
+                           int32_t k_pos) {
+  if ((op != CSA2_OP_INDEX_FULL && op != CSA2_OP_INDEX_REINDEX) || n_rows < 1 || max_nvis < 0 ||
+      k_blocks < 0 || k_blocks > kMaxBlocks || k_pos < 1 || k_pos > kMaxPos)
+    return 0;
+  return plan_workspace(op, n_rows, max_nvis, k_blocks, k_pos).total;
+}
+
+csa2_status csa2_index_full(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                            const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                            int32_t max_nvis, int32_t k_blocks, int32_t k_pos,
+                            int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
+                            int32_t *n_topk, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  return run_indexer(CSA2_OP_INDEX_FULL, cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis,
+                     nullptr, nullptr, k_blocks, k_pos, pool_blocks, n_pool, topk, n_topk,
+                     workspace, workspace_bytes, stream);
+}
+
+csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                               const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                               int32_t max_nvis, const int32_t *pool_blocks,
+                               const int32_t *n_pool, int32_t k_blocks, int32_t k_pos,
+                               int32_t *topk, int32_t *n_topk, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  const int32_t kb = pool_blocks ? k_blocks : 0;
+  if (pool_blocks && k_blocks < 1) return CSA2_E_INVALID_ARG;
+  return run_indexer(CSA2_OP_INDEX_REINDEX, cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis,
+                     pool_blocks, n_pool, kb, k_pos, nullptr, nullptr, topk, n_topk, workspace,
+                     workspace_bytes, stream);
+}
+
+csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
+                             const int32_t *row_seq, int32_t n_rows, const int32_t *topk,
+                             const int32_t *n_topk, int32_t k_pos, float scale,
+                             const csa2_swa *swa, float *o, float *lse, void *stream) {
+  if (!cache_ok(cache, true, false)) return CSA2_E_INVALID_ARG;
+  if (!q || !row_seq || !topk || !n_topk || !o || !lse) return CSA2_E_INVALID_ARG;
+  if (n_rows < 0 || k_pos < 1 || !isfinite(scale)) return CSA2_E_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(o, 4) || !aligned(lse, 4)) return CSA2_E_INVALID_ARG;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64) return CSA2_E_UNSUPPORTED;
+  if (k_pos > kMaxAttnPos) return CSA2_E_UNSUPPORTED;
+  if (swa && !swa_ok(swa)) return CSA2_E_INVALID_ARG;
+  if (n_rows == 0) return CSA2_OK;
+  if (prepare() != hipSuccess) return CSA2_E_HIP;
+  AttnArgs a = {};
+  a.kv_codes = cache->kv_codes;
+  a.kv_scales = cache->kv_scales;
+  a.cap = cache->cap;
+  a.n_seq = cache->n_seq;
+  a.q = q;
+  a.row_seq = row_seq;
+  a.topk = topk;
+  a.n_topk = n_topk;
+  a.k_pos = k_pos;
+  if (swa) {
+    a.swa_kv = swa->kv;
+    a.swa_len = swa->len;
+    a.swa_end = swa->row_end;
+    a.swa_window = swa->window;
+  }
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o = o;
+  a.lse = lse;
+  a.merge_in = 0;
+  hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
+csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *row_seq,
+                           int32_t n_rows, const csa2_swa *swa, int32_t n_seq, float scale,
+                           float *o, float *lse, void *stream) {
+  if (!q || !row_seq || !o || !lse || !swa_ok(swa)) return CSA2_E_INVALID_ARG;
+  if (n_rows < 0 || n_seq < 1 || !isfinite(scale)) return CSA2_E_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(o, 4) || !aligned(lse, 4)) return CSA2_E_INVALID_ARG;
+  if (n_heads != 16 && n_heads != 32 && n_heads != 64) return CSA2_E_UNSUPPORTED;
+  if (n_rows == 0) return CSA2_OK;
+  if (prepare() != hipSuccess) return CSA2_E_HIP;
+  AttnArgs a = {};
+  a.cap = 1;
+  a.n_seq = n_seq;
+  a.q = q;
+  a.row_seq = row_seq;
+  a.swa_kv = swa->kv;
+  a.swa_len = swa->len;
+  a.swa_end = swa->row_end;
+  a.swa_window = swa->window;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o = o;
+  a.lse = lse;
+  a.merge_in = 1;
+  hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
+const char *csa2_status_string(csa2_status status) {
+  switch (status) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_E_INVALID_ARG: return "CSA2_E_INVALID_ARG: invalid argument";
+    case CSA2_E_UNSUPPORTED: return "CSA2_E_UNSUPPORTED: shape or size not supported";
+    case CSA2_E_WORKSPACE: return "CSA2_E_WORKSPACE: workspace missing, misaligned or too small";
+    case CSA2_E_HIP: return "CSA2_E_HIP: HIP runtime error";
+  }
+  return "CSA2: unknown status";
+}
+
+const char *csa2_version(void) { return "csa2 0.1.0 gfx950"; }
+
+}  // extern "C"

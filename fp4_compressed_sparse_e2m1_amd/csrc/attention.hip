@@ -1,0 +1,334 @@
+// S5 + S6: sparse attention over the selected FP4 latents, with the SWA branch
+// folded into the same softmax or merged onto an earlier result.
+//
+// [P1 "무엇과 다른가": every CSA2 mode attends with its own global Q over the
+// Top-K of the main KV; P3 "레이어 40개 가운데 4개만 전역 캐시를 만듭니다": the
+// main KV is a 512-channel latent; P3 "전역 어텐션과 지역 어텐션": a 128-token
+// sliding-window branch; P3 "4비트로 적어도 되는 이유": the SWA cache is FP8.]
+// The latent is shared by all heads and is both key and value (one latent per
+// entry, no separate V in the 356-B entry).
+//
+// One work-group (4 waves) handles one query row and all of its heads.  Keys
+// are consumed in tiles of 32 (two blocks of 16).  Wave w owns the channel
+// quarter [128w, 128w+128):
+//   * it gathers only its quarter of each key (16 B of E2M1 codes + 2 scale
+//     bytes, or 32 B of E4M3 for SWA rows) and dequantises it once, exactly,
+//     to f16;
+//   * Q.K^T: it computes the partial logits over its quarter with 16x16x32
+//     MFMAs (rows = 16 heads, columns = 16 keys); the four partials are summed
+//     through LDS;
+//   * P.V: it writes its dequantised quarter transposed into LDS and
+//     accumulates O[:, quarter] with MFMAs (rows = 16 heads, columns = 16
+//     channels, contraction = the 32 keys of the tile).
+// The softmax is the online (running max) form in base 2; the running max is
+// only raised when a tile's maximum exceeds it by more than 2^8, so most tiles
+// skip the rescale of O.  Probabilities enter the P.V product in f16 and the
+// normaliser sums the same rounded values, so the weights stay normalised.
+#include "device.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kTileKeys = 32;
+constexpr int kVtStride = 40;          // halves per Vt row (32 keys + pad)
+constexpr int kPStride = 40;           // halves per P row
+constexpr float kLazyRescale = 8.0f;   // log2 units
+
+struct RawTile {
+  uint4 a[2];       // FP4: codes of the quarter; SWA: bytes 0..15 of the quarter
+  uint4 b[2];       // SWA: bytes 16..31
+  uint32_t sc[2];   // FP4: two scale bytes
+  bool valid[2];
+};
+
+template <int HB>
+__global__ void __launch_bounds__(kAttnThreads)
+attn_kernel(AttnArgs a) {
+  static_assert(HB == 1 || HB == 2 || HB == 4, "heads must be 16, 32 or 64");
+  constexpr int H = 16 * HB;
+  constexpr int TPH = kAttnThreads / H;        // softmax threads per head
+  constexpr int KPT = kTileKeys / TPH;         // keys per softmax thread
+
+  __shared__ __attribute__((aligned(16))) float s_part[4][kTileKeys][H];
+  __shared__ __attribute__((aligned(16))) _Float16 s_vt[512 * kVtStride];
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[H * kPStride];
+  __shared__ __attribute__((aligned(16))) float s_alpha[H];
+  __shared__ float s_m[H], s_l[H];
+  __shared__ int s_valid[kTileKeys];
+  __shared__ int s_rescale;
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int G = lane >> 4;
+  const int c = lane & 15;
+
+  int seq = a.row_seq[r];
+  const bool seq_ok = seq >= 0 && seq < a.n_seq;
+  if (!seq_ok) seq = 0;
+  int n_g = 0;
+  if (a.topk && seq_ok) {
+    n_g = a.n_topk[r];
+    n_g = n_g < 0 ? 0 : (n_g > a.k_pos ? a.k_pos : n_g);
+  }
+  int64_t s0 = 0;
+  int n_s = 0;
+  if (a.swa_kv && seq_ok) {
+    int64_t end = a.swa_end[r];
+    end = end < 0 ? 0 : (end > a.swa_len ? a.swa_len : end);
+    s0 = end - a.swa_window;
+    s0 = s0 < 0 ? 0 : s0;
+    n_s = (int)(end - s0);
+  }
+  const int n_gt = (n_g + kTileKeys - 1) / kTileKeys;
+  const int n_tiles = n_gt + (n_s + kTileKeys - 1) / kTileKeys;
+
+  // Q operand: qa[hb][t] = q[r][16hb + c][128w + 32G + 8t .. +7] in f16.
+  f16x8 qa[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * H + 16 * hb + c) * 512 +
+                                                      128 * w + 32 * G);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[hb][t] = bf16x8_to_f16(qp[t]);
+  }
+
+  // Running state.  O[hb][db]: lane (G, c) holds heads 16hb + 4G + i (i < 4)
+  // at channel 128w + 16db + c.
+  f32x4 acc_o[HB][8];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc_o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.merge_in) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * hb + 4 * G + i;
+        const float lin = a.lse[(int64_t)r * H + h];
+        if (lin != -INFINITY) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+            acc_o[hb][db][i] = a.o[((int64_t)r * H + h) * 512 + 128 * w + 16 * db + c];
+        }
+      }
+  }
+  if (tid < H) {
+    float m0 = -INFINITY, l0 = 0.f;
+    if (a.merge_in) {
+      const float lin = a.lse[(int64_t)r * H + tid];
+      if (lin != -INFINITY) {
+        m0 = lin * 1.4426950408889634f;
+        l0 = 1.f;
+      }
+    }
+    s_m[tid] = m0;
+    s_l[tid] = l0;
+  }
+
+  const uint8_t *kv_codes = a.kv_codes + (int64_t)seq * a.cap * 256;
+  const uint8_t *kv_scales = a.kv_scales + (int64_t)seq * a.cap * 32;
+  const uint8_t *swa = a.swa_kv ? a.swa_kv + ((int64_t)seq * a.swa_len) * 512 : nullptr;
+  const int32_t *topk = a.topk ? a.topk + (int64_t)r * a.k_pos : nullptr;
+
+  auto load_tile = [&](int tile) {
+    RawTile t;
+    if (tile < n_gt) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int slot = tile * kTileKeys + 16 * kb + c;
+        int64_t e = -1;
+        if (slot < n_g) e = topk[slot];
+        const bool ok = e >= 0 && e < a.cap;
+        t.valid[kb] = ok;
+        const int64_t el = ok ? e : 0;
+        t.a[kb] = *reinterpret_cast<const uint4 *>(kv_codes + el * 256 + 64 * w + 16 * G);
+        t.sc[kb] = *reinterpret_cast<const uint16_t *>(kv_scales + el * 32 + 8 * w + 2 * G);
+        t.b[kb] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int slot = (tile - n_gt) * kTileKeys + 16 * kb + c;
+        const bool ok = slot < n_s;
+        t.valid[kb] = ok;
+        const int64_t row = ok ? s0 + slot : 0;
+        const uint4 *p = reinterpret_cast<const uint4 *>(swa + row * 512 + 128 * w + 32 * G);
+        t.a[kb] = p[0];
+        t.b[kb] = p[1];
+        t.sc[kb] = 0;
+      }
+    }
+    return t;
+  };
+
+  RawTile cur;
+  if (n_tiles > 0) cur = load_tile(0);
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    RawTile nxt;
+    if (tile + 1 < n_tiles) nxt = load_tile(tile + 1);
+    const bool is_swa = tile >= n_gt;
+
+    // dequantise this wave's quarter of the 32 keys
+    f16x8 kf[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (!is_swa) {
+        const _Float16 sa = e4m3_to_f16(cur.sc[kb] & 0xFFu);
+        const _Float16 sb = e4m3_to_f16((cur.sc[kb] >> 8) & 0xFFu);
+        const f16x8 va = f16x8{sa, sa, sa, sa, sa, sa, sa, sa};
+        const f16x8 vb = f16x8{sb, sb, sb, sb, sb, sb, sb, sb};
+        kf[kb][0] = e2m1x8_to_f16(cur.a[kb].x) * va;
+        kf[kb][1] = e2m1x8_to_f16(cur.a[kb].y) * va;
+        kf[kb][2] = e2m1x8_to_f16(cur.a[kb].z) * vb;
+        kf[kb][3] = e2m1x8_to_f16(cur.a[kb].w) * vb;
+      } else {
+        kf[kb][0] = e4m3x8_to_f16(cur.a[kb].x, cur.a[kb].y);
+        kf[kb][1] = e4m3x8_to_f16(cur.a[kb].z, cur.a[kb].w);
+        kf[kb][2] = e4m3x8_to_f16(cur.b[kb].x, cur.b[kb].y);
+        kf[kb][3] = e4m3x8_to_f16(cur.b[kb].z, cur.b[kb].w);
+      }
+      if (!cur.valid[kb]) {
+        // skipped slots load entry 0; zero them so no stale byte pattern
+        // (e.g. a NaN code in an unwritten row) can reach the P.V product
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kf[kb][t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    if (w == 0 && G == 0) {
+      s_valid[c] = cur.valid[0];
+      s_valid[16 + c] = cur.valid[1];
+    }
+    if (tid == 0) s_rescale = 0;
+
+    // partial logits over this wave's channel quarter
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s = mfma16x16x32(qa[hb][t], kf[kb][t], s);
+        *reinterpret_cast<float4 *>(&s_part[w][16 * kb + c][16 * hb + 4 * G]) =
+            make_float4(s[0], s[1], s[2], s[3]);
+      }
+    // transposed copy of the dequantised quarter: s_vt[channel][key]
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          s_vt[(128 * w + 32 * G + 8 * t + e) * kVtStride + 16 * kb + c] = kf[kb][t][e];
+    __syncthreads();
+
+    // online softmax: thread -> head h, keys kk0 .. kk0 + KPT - 1
+    {
+      const int h = tid / TPH;
+      const int kk0 = (tid % TPH) * KPT;
+      float sv[KPT];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int kk = kk0 + j;
+        float s = (s_part[0][kk][h] + s_part[1][kk][h]) + (s_part[2][kk][h] + s_part[3][kk][h]);
+        s = s_valid[kk] ? s * a.scale_log2 : -INFINITY;
+        sv[j] = s;
+        tmax = fmaxf(tmax, s);
+      }
+#pragma unroll
+      for (int off = TPH / 2; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+      const float m_old = s_m[h];
+      const float l_old = s_l[h];
+      float m_new = m_old;
+      if (m_old == -INFINITY || tmax > m_old + kLazyRescale) m_new = fmaxf(tmax, m_old);
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const float p = (m_new == -INFINITY) ? 0.f : exp2f(sv[j] - m_new);
+        const _Float16 ph = (_Float16)p;
+        s_p[h * kPStride + kk0 + j] = ph;
+        psum += (float)ph;
+      }
+#pragma unroll
+      for (int off = TPH / 2; off > 0; off >>= 1) psum += __shfl_xor(psum, off);
+      const float alpha = (m_old == -INFINITY || m_new == m_old) ? 1.f : exp2f(m_old - m_new);
+      if ((tid % TPH) == 0) {
+        s_m[h] = m_new;
+        s_l[h] = l_old * alpha + psum;
+        s_alpha[h] = alpha;
+        if (alpha != 1.f) s_rescale = 1;
+      }
+    }
+    __syncthreads();
+
+    // O[:, quarter] = alpha * O + P V
+    if (s_rescale) {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const float4 al = *reinterpret_cast<const float4 *>(&s_alpha[16 * hb + 4 * G]);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          acc_o[hb][db][0] *= al.x;
+          acc_o[hb][db][1] *= al.y;
+          acc_o[hb][db][2] *= al.z;
+          acc_o[hb][db][3] *= al.w;
+        }
+      }
+    }
+    f16x8 vb[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      vb[db] = *reinterpret_cast<const f16x8 *>(&s_vt[(128 * w + 16 * db + c) * kVtStride + 8 * G]);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const f16x8 pa = *reinterpret_cast<const f16x8 *>(&s_p[(16 * hb + c) * kPStride + 8 * G]);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc_o[hb][db] = mfma16x16x32(pa, vb[db], acc_o[hb][db]);
+    }
+    __syncthreads();
+    cur = nxt;
+  }
+
+  __syncthreads();
+  // normalise and store
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * hb + 4 * G + i;
+      const float l = s_l[h];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float *orow = a.o + ((int64_t)r * H + h) * 512 + 128 * w + c;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) orow[16 * db] = acc_o[hb][db][i] * inv;
+    }
+  }
+  if (tid < H) {
+    const float l = s_l[tid];
+    a.lse[(int64_t)r * H + tid] =
+        l > 0.f ? (s_m[tid] + log2f(l)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t prepare_attention() { return hipSuccess; }
+
+hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  dim3 grid((unsigned)n_rows);
+  switch (n_heads) {
+    case 16: attn_kernel<1><<<grid, kAttnThreads, 0, stream>>>(a); break;
+    case 32: attn_kernel<2><<<grid, kAttnThreads, 0, stream>>>(a); break;
+    default: attn_kernel<4><<<grid, kAttnThreads, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa2

@@ -1,0 +1,79 @@
+// Device helpers shared by the CSA2 kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Order-preserving map fp32 -> uint32 (larger score -> larger key).  Key 0 is
+// reserved for "no candidate": every non-NaN float maps above it (-inf maps to
+// 0x007FFFFF), so a selection never picks a 0 key.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Eight E2M1 codes (one dword, channel 2k in the low nibble of byte k) ->
+// eight fp16 values in channel order.  The gfx950 scaled conversion applies
+// only the exponent of its fp32 scale, so it is used with scale 1.0 (exact)
+// and the E4M3 block scale is applied separately.
+__device__ __forceinline__ f16x8 e2m1x8_to_f16(uint32_t w) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Four E4M3FN bytes of one dword -> four fp16 values (exact, unit scale).
+__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, _Float16 *out) {
+  f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// Eight E4M3FN bytes (two dwords, element order) -> f16x8.
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t w0, uint32_t w1) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// One E4M3FN byte (in the low 8 bits) -> fp16 (exact).
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t byte) {
+  f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte, 1.0f, false);
+  return v[0];
+}
+
+// bf16 bit pattern -> fp16.  Exact for |v| in [2^-14, 65504] (normal fp16);
+// smaller magnitudes round to the fp16 subnormal grid (2^-24 spacing).
+__device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b) {
+  return (_Float16)__uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ f16x8 bf16x8_to_f16(uint4 v) {
+  return f16x8{bf16_to_f16(v.x & 0xFFFF), bf16_to_f16(v.x >> 16), bf16_to_f16(v.y & 0xFFFF),
+               bf16_to_f16(v.y >> 16),    bf16_to_f16(v.z & 0xFFFF), bf16_to_f16(v.z >> 16),
+               bf16_to_f16(v.w & 0xFFFF), bf16_to_f16(v.w >> 16)};
+}
+
+// D = A(16x32) * B(32x16) + C on the matrix cores.  Lane l holds
+// A[l % 16][8*(l/16) .. +7], B[8*(l/16) .. +7][l % 16] and
+// C[4*(l/16) .. +3][l % 16].
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace csa2

@@ -1,0 +1,362 @@
+// S2-S4: indexer scoring and Top-K selection.
+//
+// Scoring [P1 "무엇과 다른가": the indexer Q scores the indexer keys, which
+// are stored next to the main KV; the first decoder Full layer scans the whole
+// visible range, later layers only the pool of 2,048 blocks x 8 positions
+// (P3 "레이어 40개 가운데 4개만 전역 캐시를 만듭니다")].  The score of entry j
+// for a query row is  sum_h w_h * max(0, q_h . k_hat_j)  over 8 heads of 128
+// dims, k_hat = E2M1 code x E4M3 scale (one scale per 32 channels).
+//
+// One wave scores 16 entries per step with four 16x16x32 f16 MFMAs:
+//   rows (M) = 16 query heads (8 real, 8 zero), columns (N) = 16 entries,
+//   contraction (K) = 128 key channels in 4 steps of 32.
+// Lane (G = lane/16, c = lane%16) loads 16 contiguous bytes of entry c's code
+// row -- channels [32G, 32G+32), exactly one scale group -- so the wave reads
+// a 1 KiB contiguous tile with one 16-byte load per lane.  MFMA step t uses
+// channels 32G + 8t .. +7 from lane group G (the contraction order is
+// permuted consistently in the query operand, which does not change the sum).
+// Each lane converts its 32 codes with the hardware E2M1 -> f16 conversion
+// (unit scale, exact) and multiplies by its group's E4M3 scale in f16
+// (exact: the product has at most 6 significant bits).  The bf16 query is
+// converted to f16 once per work-group.  Products are exact in the MFMA and
+// accumulate in fp32.
+//
+// Selection: scores are mapped to order-preserving uint32 keys (0 = no
+// candidate).  A work-group loads up to 16,384 keys of one row into LDS and
+// runs a 4-pass 8-bit radix select for the k-th largest key, then an ordered
+// compaction writes the kept positions in ascending order (ties at the
+// threshold go to the lowest positions).  Rows with more keys are cut into
+// chunks whose Top-k survivors feed a further level, which keeps the result
+// exact because a global Top-k element is in its chunk's Top-k.
+#include "device.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kTilesPerWave = kScoreChunk / (4 * 16);   // 16 tiles of 16 entries
+
+template <int MODE>
+__global__ void __launch_bounds__(kScoreThreads)
+score_kernel(ScoreArgs a) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int G = lane >> 4;
+  const int c = lane & 15;
+
+  int seq = a.row_seq[r];
+  int n_vis = a.row_nvis[r];
+  n_vis = n_vis < 0 ? 0 : (n_vis > a.max_nvis ? a.max_nvis : n_vis);
+  if (seq < 0 || seq >= a.n_seq) {
+    seq = 0;
+    n_vis = 0;
+  }
+  int np = 0;
+  if (MODE == kScorePool) {
+    np = a.n_pool[r];
+    np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
+  }
+  // slots of this row: entries (scan / flat) or candidate slots (pool)
+  const int64_t n_slots = (MODE == kScorePool) ? (int64_t)8 * a.k_blocks : (int64_t)n_vis;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kScoreChunk;
+  if (chunk0 >= n_slots) return;
+
+  // Query operand: lane (G, c) holds head c's channels 32G + 8t .. +7, t = 0..3.
+  f16x8 qa[4];
+  if (c < 8) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q_idx + ((int64_t)r * 8 + c) * 128 + 32 * G);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[t] = bf16x8_to_f16(qp[t]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  float wh[4] = {0.f, 0.f, 0.f, 0.f};
+  if (G < 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wh[i] = a.w[(int64_t)r * 8 + 4 * G + i];
+  }
+
+  const uint8_t *codes_base = a.ik_codes + (int64_t)seq * a.cap * 64;
+  const uint8_t *scales_base = a.ik_scales + (int64_t)seq * a.cap * 4;
+  uint32_t *out_row = a.keys_out + (int64_t)r * a.out_stride;
+
+  const int64_t wave0 = chunk0 + (int64_t)wave * kTilesPerWave * 16;
+  constexpr int U = 4;
+  for (int tb = 0; tb < kTilesPerWave; tb += U) {
+    if (wave0 + (int64_t)tb * 16 >= n_slots) break;
+    uint4 craw[U];
+    uint32_t sraw[U];
+    int64_t slot[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      slot[u] = wave0 + (int64_t)(tb + u) * 16 + c;
+      int64_t entry;
+      if (MODE == kScorePool) {
+        const int64_t p = slot[u] >> 3;
+        int b = -1;
+        if (p < np) b = a.pool_blocks[(int64_t)r * a.k_blocks + p];
+        entry = (int64_t)b * 8 + (slot[u] & 7);
+        valid[u] = (p < np) && b >= 0 && entry < n_vis;
+      } else {
+        entry = slot[u];
+        valid[u] = entry < n_vis;
+      }
+      const int64_t e_ld = valid[u] ? entry : 0;
+      craw[u] = *reinterpret_cast<const uint4 *>(codes_base + e_ld * 64 + 16 * G);
+      sraw[u] = scales_base[e_ld * 4 + G];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const _Float16 s = e4m3_to_f16(sraw[u]);
+      const f16x8 sv = f16x8{s, s, s, s, s, s, s, s};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16x16x32(qa[0], e2m1x8_to_f16(craw[u].x) * sv, acc);
+      acc = mfma16x16x32(qa[1], e2m1x8_to_f16(craw[u].y) * sv, acc);
+      acc = mfma16x16x32(qa[2], e2m1x8_to_f16(craw[u].z) * sv, acc);
+      acc = mfma16x16x32(qa[3], e2m1x8_to_f16(craw[u].w) * sv, acc);
+      // lane (G, c): d[head 4G + i][entry c]; heads 8..15 are zero padding
+      float part = wh[0] * fmaxf(acc[0], 0.f) + wh[1] * fmaxf(acc[1], 0.f);
+      part += wh[2] * fmaxf(acc[2], 0.f) + wh[3] * fmaxf(acc[3], 0.f);
+      const float score = part + __shfl_down(part, 16);   // heads 0..3 + heads 4..7
+      if (MODE == kScoreBlockMax) {
+        float m = valid[u] ? score : -INFINITY;
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        const int64_t blk = slot[u] >> 3;
+        if (lane < 16 && (c & 7) == 0 && blk * 8 < n_slots) out_row[blk] = score_key(m);
+      } else if (MODE == kScoreFlat) {
+        if (lane < 16 && valid[u]) out_row[slot[u]] = score_key(score);
+      } else {
+        if (lane < 16 && slot[u] < n_slots) out_row[slot[u]] = valid[u] ? score_key(score) : 0u;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- selection
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+template <bool FINAL>
+__global__ void __launch_bounds__(kSelThreads)
+select_kernel(SelectArgs a) {
+  extern __shared__ uint32_t skeys[];
+  __shared__ uint32_t hist[256];
+  __shared__ int s_red[kSelWaves * 2];
+  __shared__ int s_digit, s_above, s_nvalid;
+
+  const int r = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  int n_row;
+  if (a.count_kind == kCountFixed) {
+    n_row = a.count_fixed;
+  } else {
+    int seq = a.row_seq[r];
+    int nv = a.row_nvis[r];
+    nv = nv < 0 ? 0 : (nv > a.max_nvis ? a.max_nvis : nv);
+    if (seq < 0 || seq >= a.n_seq) nv = 0;
+    n_row = (a.count_kind == kCountNvis) ? nv : (nv + 7) / 8;
+  }
+  const int64_t start = (int64_t)chunk * kSelectChunk;
+  int n = (int)((int64_t)n_row - start);
+  n = n < 0 ? 0 : (n > kSelectChunk ? kSelectChunk : n);
+
+  // load keys, count the valid (non-zero) ones
+  const uint32_t *kin = a.keys_in + (int64_t)r * a.in_stride + start;
+  int nvalid = 0;
+  for (int i = tid; i < n; i += kSelThreads) {
+    const uint32_t k = kin[i];
+    skeys[i] = k;
+    nvalid += (k != 0u);
+  }
+  if (tid < 256) hist[tid] = 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) nvalid += __shfl_xor(nvalid, off);
+  if (lane == 0) s_red[wave] = nvalid;
+  __syncthreads();
+  if (tid == 0) {
+    int t = 0;
+    for (int i = 0; i < kSelWaves; ++i) t += s_red[i];
+    s_nvalid = t;
+  }
+  __syncthreads();
+  nvalid = s_nvalid;
+  const int k_eff = nvalid < a.k ? nvalid : a.k;
+
+  // radix select of the k_eff-th largest key
+  uint32_t thr = 0u;
+  int k_eq = 0;
+  if (k_eff < nvalid) {
+    uint32_t prefix = 0u, mask = 0u;
+    int k_rem = k_eff;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < n; i += kSelThreads) {
+        const uint32_t k = skeys[i];
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l owns bins 255-4l .. 252-4l (descending)
+        int cnt[4];
+        int local = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cnt[j] = (int)hist[255 - 4 * lane - j];
+          local += cnt[j];
+        }
+        const int incl = wave_incl_scan(local, lane);
+        const int excl = incl - local;
+        if (excl < k_rem && k_rem <= incl) {
+          int cum = excl;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (cum + cnt[j] >= k_rem) {
+              s_digit = 255 - 4 * lane - j;
+              s_above = cum;
+              break;
+            }
+            cum += cnt[j];
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      mask |= 255u << shift;
+      k_rem -= s_above;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+    }
+    thr = prefix;
+    k_eq = k_rem;
+  }
+
+  // ordered compaction: thread tid owns positions [tid*per, (tid+1)*per)
+  const int per = (n + kSelThreads - 1) / kSelThreads;
+  const int b0 = tid * per;
+  const int b1 = (b0 + per < n) ? b0 + per : n;
+  int gt = 0, eq = 0;
+  for (int i = b0; i < b1; ++i) {
+    const uint32_t k = skeys[i];
+    gt += (k > thr);
+    eq += (k == thr);
+  }
+  const int gt_in = wave_incl_scan(gt, lane);
+  const int eq_in = wave_incl_scan(eq, lane);
+  if (lane == 63) {
+    s_red[wave] = gt_in;
+    s_red[kSelWaves + wave] = eq_in;
+  }
+  __syncthreads();
+  int gt_base = 0, eq_base = 0;
+  for (int i = 0; i < wave; ++i) {
+    gt_base += s_red[i];
+    eq_base += s_red[kSelWaves + i];
+  }
+  int eq_rank = eq_base + eq_in - eq;
+  int pos = gt_base + gt_in - gt + (eq_rank < k_eq ? eq_rank : k_eq);
+
+  const int32_t *idin = a.ids_in ? a.ids_in + (int64_t)r * a.in_stride + start : nullptr;
+  if (FINAL) {
+    int32_t *out = a.out + (int64_t)r * a.k;
+    int np = 0;
+    if (a.map_kind == kMapPool) {
+      np = a.n_pool[r];
+      np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
+    }
+    for (int i = b0; i < b1; ++i) {
+      const uint32_t k = skeys[i];
+      bool take = k > thr;
+      if (k == thr) {
+        take = eq_rank < k_eq;
+        ++eq_rank;
+      }
+      if (take) {
+        int id = idin ? idin[i] : (int)(start + i);
+        if (a.map_kind == kMapPool) {
+          const int p = id >> 3;
+          const int b = (p < np) ? a.pool_blocks[(int64_t)r * a.k_blocks + p] : -1;
+          id = b * 8 + (id & 7);
+        }
+        out[pos++] = id;
+      }
+    }
+    for (int i = k_eff + tid; i < a.k; i += kSelThreads) out[i] = -1;
+    if (tid == 0) a.n_out[r] = k_eff;
+  } else {
+    uint32_t *kout = a.keys_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
+    int32_t *iout = a.ids_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
+    for (int i = b0; i < b1; ++i) {
+      const uint32_t k = skeys[i];
+      bool take = k > thr;
+      if (k == thr) {
+        take = eq_rank < k_eq;
+        ++eq_rank;
+      }
+      if (take) {
+        kout[pos] = k;
+        iout[pos] = idin ? idin[i] : (int)(start + i);
+        ++pos;
+      }
+    }
+    for (int i = k_eff + tid; i < a.k; i += kSelThreads) {
+      kout[i] = 0u;
+      iout[i] = -1;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int64_t slots,
+                        hipStream_t stream) {
+  const int64_t chunks = (slots + kScoreChunk - 1) / kScoreChunk;
+  if (chunks == 0 || n_rows == 0) return hipSuccess;
+  dim3 grid((unsigned)chunks, (unsigned)n_rows);
+  switch (mode) {
+    case kScoreBlockMax: score_kernel<kScoreBlockMax><<<grid, kScoreThreads, 0, stream>>>(a); break;
+    case kScoreFlat: score_kernel<kScoreFlat><<<grid, kScoreThreads, 0, stream>>>(a); break;
+    default: score_kernel<kScorePool><<<grid, kScoreThreads, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t prepare_select() {
+  const int bytes = kSelectChunk * (int)sizeof(uint32_t);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<false>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
+                         hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  dim3 grid((unsigned)n_chunks, (unsigned)n_rows);
+  const size_t lds = (size_t)kSelectChunk * sizeof(uint32_t);
+  if (final_level)
+    select_kernel<true><<<grid, kSelThreads, lds, stream>>>(a);
+  else
+    select_kernel<false><<<grid, kSelThreads, lds, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

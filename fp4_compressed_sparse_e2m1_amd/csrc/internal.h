@@ -1,0 +1,98 @@
+// Internal interfaces between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// ---------------------------------------------------------------- indexer
+enum ScoreMode { kScoreBlockMax = 0, kScoreFlat = 1, kScorePool = 2 };
+
+struct ScoreArgs {
+  const uint8_t *ik_codes;    // [n_seq][cap][64]
+  const uint8_t *ik_scales;   // [n_seq][cap][4]
+  int64_t cap;
+  int32_t n_seq;
+  const uint16_t *q_idx;      // bf16 [R][8][128]
+  const float *w;             // [R][8]
+  const int32_t *row_seq;     // [R]
+  const int32_t *row_nvis;    // [R]
+  int32_t max_nvis;
+  const int32_t *pool_blocks; // [R][k_blocks]  (pool mode)
+  const int32_t *n_pool;      // [R]            (pool mode)
+  int32_t k_blocks;
+  uint32_t *keys_out;         // [R][out_stride] order-preserving score keys
+  int64_t out_stride;
+};
+
+// Entries per work-group of the scoring kernel.
+constexpr int kScoreChunk = 1024;
+
+hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int64_t slots,
+                        hipStream_t stream);
+
+enum CountKind { kCountFixed = 0, kCountNvis = 1, kCountNvisBlocks = 2 };
+enum MapKind { kMapId = 0, kMapPool = 1 };
+
+struct SelectArgs {
+  const uint32_t *keys_in;    // [R][in_stride]
+  const int32_t *ids_in;      // [R][in_stride] or null (id = position)
+  int64_t in_stride;
+  int32_t count_kind;
+  int32_t count_fixed;
+  const int32_t *row_seq;
+  const int32_t *row_nvis;
+  int32_t n_seq;
+  int32_t max_nvis;
+  int32_t k;
+  // intermediate level outputs: [R][n_chunks * k], zero-keyed holes
+  uint32_t *keys_out;
+  int32_t *ids_out;
+  int64_t out_stride;
+  // final level outputs
+  int32_t *out;               // [R][k], ascending, -1 padded
+  int32_t *n_out;             // [R]
+  int32_t map_kind;
+  const int32_t *pool_blocks; // [R][k_blocks] (map_kind == kMapPool)
+  const int32_t *n_pool;
+  int32_t k_blocks;
+};
+
+// Keys held in LDS by one selection work-group.
+constexpr int kSelectChunk = 16384;
+
+hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
+                         hipStream_t stream);
+hipError_t prepare_select();
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const uint8_t *kv_codes;    // [n_seq][cap][256]
+  const uint8_t *kv_scales;   // [n_seq][cap][32]
+  int64_t cap;
+  int32_t n_seq;
+  const uint16_t *q;          // bf16 [R][H][512]
+  const int32_t *row_seq;
+  const int32_t *topk;        // [R][k_pos] or null (no global keys)
+  const int32_t *n_topk;
+  int32_t k_pos;
+  const uint8_t *swa_kv;      // [n_seq][swa_len][512] E4M3 or null
+  int64_t swa_len;
+  const int32_t *swa_end;
+  int32_t swa_window;
+  float scale_log2;           // softmax scale * log2(e)
+  float *o;                   // [R][H][512]
+  float *lse;                 // [R][H]
+  int32_t merge_in;           // 1: start from (o, lse) as an earlier result
+};
+
+hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, hipStream_t stream);
+hipError_t prepare_attention();
+
+// ---------------------------------------------------------------- quantise
+hipError_t launch_quantize(const float *x, int64_t n, int dim, int group, const int64_t *dst_rows,
+                           uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+}  // namespace csa2

@@ -1,0 +1,222 @@
+/*
+ * libcsa2 -- CSA2 (Compressed Sparse Attention 2) hot path for AMD MI355X
+ * (gfx950), C ABI.
+ *
+ * The library implements the global-attention path of a CSA2 layer as the
+ * pages describe it:
+ *   - P1: onedev.kr digest "KV 캐시를 토큰당 890바이트로 압축한 552B 멀티모달
+ *     MoE, DeepSeek-V4.1-Flash", section "무엇과 다른가" (how it differs):
+ *     the Full / Reindex / Reuse layer modes, the FP4 global KV cache and the
+ *     hierarchical sparse indexer;
+ *   - P3: genexis.ai explainer "100만 토큰을 0.9GB에, 딥시크 V4.1 논문이 KV
+ *     캐시를 줄인 방법", sections "레이어 40개 가운데 4개만 전역 캐시를
+ *     만듭니다" (entry layout, 2,048 blocks of 8, Top-512), "4비트로 적어도
+ *     되는 이유" (FP4 with one 8-bit scale per 16 values, FP8 SWA cache) and
+ *     "전역 어텐션과 지역 어텐션" (the 128-token SWA branch).
+ *
+ * A layer in each mode is a sequence of calls:
+ *   Full    = csa2_quantize_fp4 (its new entries, both planes)
+ *             + csa2_index_full + csa2_sparse_attn [+ csa2_swa_merge]
+ *   Reindex = csa2_index_reindex (on the Full layer's cache and pool)
+ *             + csa2_sparse_attn [+ csa2_swa_merge]
+ *   Reuse   = csa2_sparse_attn [+ csa2_swa_merge] on the inherited Top-K.
+ * csa2_sparse_attn can fold the SWA branch into the same softmax (pass a
+ * csa2_swa); csa2_swa_merge adds it to an earlier global-only result.
+ *
+ * Conventions for every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller (for
+ *     example a torch tensor's storage); struct arguments are host pointers
+ *     to structs that hold device pointers.  The library allocates no memory,
+ *     keeps no pointer after it returns, and holds no mutable global state;
+ *     scratch memory is the caller's `workspace`, sized by
+ *     csa2_workspace_size().
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued on it; CSA2_OK means "validated and enqueued".  Device faults
+ *     show up at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched; on an
+ *     error status nothing has been written or launched.
+ *   - Device-side counts (row_nvis, n_pool, n_topk, SWA ends) are clamped to
+ *     the host-side maxima; out-of-range sequence ids make a row empty;
+ *     entry ids outside [0, cap) are skipped.  These guards keep every access
+ *     in bounds; such inputs are still outside the contract.
+ *   - Results are deterministic: fixed reduction orders, Top-K lists sorted
+ *     ascending.
+ *   - NaN or infinite inputs are outside the contract.
+ *
+ * Data layout in HBM (one plane per field, struct-of-arrays):
+ *   kv_codes  [n_seq][cap][256] uint8   main latent, 512 E2M1 codes
+ *   kv_scales [n_seq][cap][32]  uint8   main latent, one E4M3FN scale per 16 ch
+ *   ik_codes  [n_seq][cap][64]  uint8   indexer key, 128 E2M1 codes
+ *   ik_scales [n_seq][cap][4]   uint8   indexer key, one E4M3FN scale per 32 ch
+ * 256 + 32 + 64 + 4 = 356 bytes per entry (P3, "레이어 40개 가운데 4개만...").
+ * E2M1 codes: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa (OCP
+ * MX); channel 2k is the low nibble of byte k, channel 2k+1 the high nibble.
+ * Scales: OCP E4M3FN (bias 7, max 448), always >= 0.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_E_INVALID_ARG = 1,  /* null pointer, negative or inconsistent size */
+    CSA2_E_UNSUPPORTED = 2,  /* valid but outside what the kernels implement */
+    CSA2_E_WORKSPACE = 3,    /* workspace missing or smaller than required */
+    CSA2_E_HIP = 4           /* a HIP runtime call or launch failed */
+} csa2_status;
+
+/* Operation ids for csa2_workspace_size(). */
+enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_INDEX_REINDEX = 2 };
+
+/* Global (compressed) KV cache of one Full layer: four device planes, laid
+ * out as in the header comment.  Entry j of sequence s lives at row
+ * s * cap + j of every plane. */
+typedef struct {
+    uint8_t *kv_codes;
+    uint8_t *kv_scales;
+    uint8_t *ik_codes;
+    uint8_t *ik_scales;
+    int64_t cap;    /* entries per sequence (>= 1) */
+    int32_t n_seq;  /* sequences (>= 1) */
+} csa2_cache;
+
+/* Sliding-window (SWA) branch of one layer [P3 "전역 어텐션과 지역 어텐션":
+ * the local branch sees the last 128 tokens; "4비트로 적어도 되는 이유":
+ * the SWA cache stays 8-bit].
+ *   kv      : device, OCP E4M3FN bytes [n_seq][len][512], unit scale; each row
+ *             is one token's 512-d SWA key, which is also its value.
+ *   len     : rows per sequence (>= 0).
+ *   row_end : device int32 [n_rows]: for query row r the window is rows
+ *             [max(0, end - window), end) of sequence row_seq[r], with end
+ *             clamped to [0, len].
+ *   window  : window length in rows, 0..1024 (128 in the pages' model). */
+typedef struct {
+    const uint8_t *kv;
+    int64_t len;
+    const int32_t *row_end;
+    int32_t window;
+} csa2_swa;
+
+/* S1 -- FP4 quantise / append [P3 "4비트로 적어도 되는 이유": NVFP4 without
+ * the second-level global scale, one 8-bit scale per 16 channels; P3
+ * "레이어 40개 가운데 4개만..." for the 512-ch latent (288 B) and the 128-d
+ * indexer key (68 B)].
+ * For each row r < n of x (fp32 [n][dim]) and each group of `group`
+ * channels: amax = max |x|; scale = E4M3FN round-to-nearest-even of amax/6
+ * (saturating at 448); each value's code = E2M1 round-to-nearest-even of
+ * |x|/scale (saturating at 6; 0 if the scale is 0), sign bit = (x < 0).
+ * Row r is written to plane row dst_rows[r] (device int64 [n]) or to row r
+ * when dst_rows is NULL:
+ *   codes  + dst * (dim/2)       (dim/2 bytes)
+ *   scales + dst * (dim/group)   (dim/group bytes).
+ * To append entry j of sequence s to a csa2_cache, use dst = s * cap + j with
+ * (dim, group) = (512, 16) on kv_* and (128, 32) on ik_*.
+ * Requires n >= 0, group in {16, 32}, dim % group == 0, 32 <= dim <= 4096. */
+csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t group,
+                              const int64_t *dst_rows, uint8_t *codes, uint8_t *scales,
+                              void *stream);
+
+/* Scratch bytes that csa2_index_full (op CSA2_OP_INDEX_FULL) or
+ * csa2_index_reindex (op CSA2_OP_INDEX_REINDEX) needs for these sizes;
+ * k_blocks = 0 selects flat mode.  Returns 0 for invalid arguments. */
+size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,
+                           int32_t k_pos);
+
+/* S2-S4 -- Full-mode indexer [P1 "무엇과 다른가": a Full layer computes its
+ * own indexer Q and selects Top-K afresh; the first decoder Full layer scans
+ * the whole causally visible range and keeps up to 2,048 blocks of 8
+ * positions as the candidate pool; P3 "레이어 40개 가운데 4개만..."].
+ * For each query row r (n_rows rows):
+ *   seq = row_seq[r], n_vis = min(row_nvis[r], max_nvis) visible entries
+ *   0..n_vis-1 of that sequence;
+ *   score(j) = sum_h w[r][h] * max(0, sum_c q_idx[r][h][c] * k_hat_j[c]),
+ *   h < 8, c < 128, k_hat = decoded indexer key (fp32 accumulation);
+ *   block mode (k_blocks > 0): block b = entries [8b, 8b+8) ∩ visible,
+ *   block score = max of its entry scores; the best min(k_blocks, #blocks)
+ *   blocks (score descending, ties to the lower block id) form the pool,
+ *   written ascending to pool_blocks[r][0..k_blocks) (-1 padded) with the
+ *   count in n_pool[r]; the pool's entries are re-scored with the same
+ *   query and the best min(k_pos, |pool entries|) positions are kept;
+ *   flat mode (k_blocks == 0, used for encoder prefill): the best k_pos of
+ *   all visible entries are kept, pool outputs are not written (may be NULL);
+ *   topk[r][0..k_pos) receives the kept entry ids ascending, -1 padded;
+ *   n_topk[r] the count.
+ * Types: q_idx bf16 bits [n_rows][8][128]; w fp32 [n_rows][8]; row_seq,
+ * row_nvis int32 [n_rows]; outputs int32.
+ * Requires 1 <= n_rows, 0 <= max_nvis <= cap, max_nvis < 2^31 - 8,
+ * 0 <= k_blocks <= 4096, 1 <= k_pos <= 4096, and workspace_bytes >=
+ * csa2_workspace_size(CSA2_OP_INDEX_FULL, n_rows, max_nvis, k_blocks, k_pos). */
+csa2_status csa2_index_full(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                            const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                            int32_t max_nvis, int32_t k_blocks, int32_t k_pos,
+                            int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
+                            int32_t *n_topk, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* S4 -- Reindex-mode indexer [P1 "무엇과 다른가": a Reindex layer reuses
+ * the earlier layer's main KV and indexer K and re-scores with its own
+ * indexer Q; P3 "레이어 40개 가운데 4개만...": it picks 512 positions inside
+ * the candidate pool, so a query never scores more than 16,384 positions].
+ * Scores, per row, the entries of the given pool (pool_blocks[r][0..n_pool[r])
+ * ascending, as csa2_index_full writes them; entries at or beyond n_vis are
+ * skipped) with this layer's q_idx and w, and keeps the best
+ * min(k_pos, #candidates) as in csa2_index_full.  pool_blocks == NULL selects
+ * flat mode (all visible entries are candidates; n_pool and k_blocks unused).
+ * Same types and limits as csa2_index_full. */
+csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                               const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                               int32_t max_nvis, const int32_t *pool_blocks,
+                               const int32_t *n_pool, int32_t k_blocks, int32_t k_pos,
+                               int32_t *topk, int32_t *n_topk, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* S5 (+S6) -- sparse attention over the selected FP4 latents [P1
+ * "무엇과 다른가": all three modes attend with their own global Q over the
+ * (possibly inherited) Top-K of the main KV; P3 "전역 어텐션과 지역 어텐션"].
+ * For each row r and head h < n_heads: the keys are the decoded 512-d main
+ * latents c_hat_j of j = topk[r][i], i < min(n_topk[r], k_pos), j >= 0 (the
+ * latent is both key and value, shared by all heads);
+ * logits = scale * (q[r][h] . c_hat_j); o[r][h] = softmax-weighted sum of
+ * the c_hat_j; lse[r][h] = natural-log log-sum-exp of the logits.
+ * With swa != NULL the window rows of the SWA branch join the same softmax
+ * (the result equals csa2_sparse_attn without swa followed by
+ * csa2_swa_merge).  With no keys at all, o = 0 and lse = -inf.
+ * Types: q bf16 bits [n_rows][n_heads][512]; topk int32 [n_rows][k_pos];
+ * n_topk int32 [n_rows]; o fp32 [n_rows][n_heads][512]; lse fp32
+ * [n_rows][n_heads].  Requires n_heads in {16, 32, 64}, n_rows >= 0,
+ * 1 <= k_pos <= 65536, scale finite. */
+csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
+                             const int32_t *row_seq, int32_t n_rows, const int32_t *topk,
+                             const int32_t *n_topk, int32_t k_pos, float scale,
+                             const csa2_swa *swa, float *o, float *lse, void *stream);
+
+/* S6 -- SWA branch and log-sum-exp merge [P3 "전역 어텐션과 지역 어텐션";
+ * the merge is the softmax over the union of the two key sets].
+ * On entry (o, lse) hold a result over some key set G (for example
+ * csa2_sparse_attn without swa; lse = -inf means G is empty).  Computes the
+ * attention of the same q over the SWA window rows S and leaves in (o, lse)
+ * the result over G ∪ S:
+ *   m = max(lse_G, lse_S); o = (e^(lse_G-m) o_G + e^(lse_S-m) o_S) /
+ *   (e^(lse_G-m) + e^(lse_S-m)); lse = m + log(e^(lse_G-m) + e^(lse_S-m)).
+ * Same types and limits as csa2_sparse_attn; swa must not be NULL. */
+csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *row_seq,
+                           int32_t n_rows, const csa2_swa *swa, int32_t n_seq, float scale,
+                           float *o, float *lse, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *csa2_status_string(csa2_status status);
+
+/* Library version, for example "csa2 0.1.0 gfx950". */
+const char *csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/csa2.h declares, and rejects invalid arguments on the host before
+anything is launched.  No call here reaches a kernel launch: every call has at
+least one argument that fails validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_compressed_sparse_e2m1_amd as csa2
+from fp4_compressed_sparse_e2m1_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000          # an aligned, non-null address that is never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    lib = csa2.load()
+    names = declared_functions()
+    assert {"csa2_quantize_fp4", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
+            "csa2_swa_merge"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
+
+
+def test_status_strings_and_version():
+    lib = csa2.load()
+    for s in range(5):
+        assert lib.csa2_status_string(s).decode().startswith("CSA2_")
+    assert "gfx950" in csa2.version()
+
+
+def test_workspace_size_rules():
+    lib = csa2.load()
+    assert lib.csa2_workspace_size(1, 8, 1 << 20, 2048, 512) > 8 * (1 << 17) * 4
+    assert lib.csa2_workspace_size(9, 8, 100, 10, 10) == 0          # unknown op
+    assert lib.csa2_workspace_size(1, 0, 100, 10, 10) == 0          # no rows
+    assert lib.csa2_workspace_size(1, 1, 100, 5000, 10) == 0        # k_blocks too large
+    assert lib.csa2_workspace_size(2, 1, 100, 0, 0) == 0            # k_pos < 1
+    # flat mode needs the per-entry keys of every row
+    assert lib.csa2_workspace_size(1, 4, 1000, 0, 16) >= 4 * 1000 * 4
+
+
+def cache_struct(cap=100, n_seq=1, null_ik=False):
+    return B._CacheStruct(FAKE, FAKE, 0 if null_ik else FAKE, FAKE, cap, n_seq)
+
+
+def test_quantize_validation():
+    lib = csa2.load()
+    f = lib.csa2_quantize_fp4
+    assert f(FAKE, -1, 512, 16, None, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 4, 512, 8, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, 520, 16, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(FAKE, 4, 16, 16, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert f(None, 4, 512, 16, None, FAKE, FAKE, None) == INVALID
+    assert f(FAKE + 4, 4, 512, 16, None, FAKE, FAKE, None) == INVALID     # misaligned x
+    assert f(FAKE, 0, 512, 16, None, None, None, None) == OK              # nothing to do
+
+
+def test_index_validation():
+    lib = csa2.load()
+    c = cache_struct()
+    full = lib.csa2_index_full
+    args = lambda **kw: dict(dict(cache=ctypes.byref(c), q=FAKE, w=FAKE, seq=FAKE, nvis=FAKE, R=2,
+                                  max_nvis=100, kb=8, kp=16, pool=FAKE, npool=FAKE, topk=FAKE,
+                                  ntopk=FAKE, ws=FAKE, wsb=0, st=None), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return full(a["cache"], a["q"], a["w"], a["seq"], a["nvis"], a["R"], a["max_nvis"], a["kb"],
+                    a["kp"], a["pool"], a["npool"], a["topk"], a["ntopk"], a["ws"], a["wsb"], a["st"])
+
+    assert call(wsb=0) == WORKSPACE                       # everything else valid
+    assert call(max_nvis=101) == INVALID                  # beyond cap
+    assert call(R=0) == INVALID
+    assert call(kp=0) == INVALID
+    assert call(kb=-1) == INVALID
+    assert call(kb=4097) == UNSUPPORTED
+    assert call(kp=5000) == UNSUPPORTED
+    assert call(q=FAKE + 2) == INVALID                    # misaligned q_idx
+    assert call(pool=None) == INVALID                     # block mode needs pool outputs
+    assert call(pool=None, npool=None, kb=0, wsb=0) == WORKSPACE   # flat mode: pool unused
+    assert call(cache=ctypes.byref(cache_struct(null_ik=True))) == INVALID
+    assert call(cache=None) == INVALID
+    need = lib.csa2_workspace_size(1, 2, 100, 8, 16)
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 8, wsb=need) == WORKSPACE       # workspace must be 256-B aligned
+    re_ = lib.csa2_index_reindex
+    assert re_(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, FAKE, None, 8, 16, FAKE, FAKE,
+               FAKE, 1 << 30, None) == INVALID            # pool without counts
+    assert re_(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, FAKE, FAKE, 0, 16, FAKE, FAKE,
+               FAKE, 1 << 30, None) == INVALID            # pool with k_blocks 0
+
+
+def test_attention_validation():
+    lib = csa2.load()
+    c = cache_struct()
+    f = lib.csa2_sparse_attn
+    base = [ctypes.byref(c), FAKE, 16, FAKE, 4, FAKE, FAKE, 512, 0.04, None, FAKE, FAKE, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(2, 24) == UNSUPPORTED                     # heads not a multiple of 16
+    assert call(2, 128) == UNSUPPORTED
+    assert call(2, 48) == UNSUPPORTED
+    assert call(7, 0) == INVALID                          # k_pos
+    assert call(8, float("inf")) == INVALID               # scale
+    assert call(1, FAKE + 2) == INVALID                   # misaligned q
+    assert call(5, None) == INVALID                       # topk
+    assert call(4, -1) == INVALID
+    bad_swa = B._SwaStruct(FAKE, 128, FAKE, 2048)         # window too long
+    assert call(9, ctypes.byref(bad_swa)) == INVALID
+    m = lib.csa2_swa_merge
+    good_swa = B._SwaStruct(FAKE, 128, FAKE, 128)
+    assert m(FAKE, 16, FAKE, 4, None, 1, 0.04, FAKE, FAKE, None) == INVALID
+    assert m(FAKE, 16, FAKE, 4, ctypes.byref(good_swa), 0, 0.04, FAKE, FAKE, None) == INVALID
+    assert m(FAKE, 20, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None) == UNSUPPORTED
+    assert m(FAKE, 16, FAKE, 0, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 512)
+    codes = torch.zeros(4, 256, dtype=torch.uint8)
+    scales = torch.zeros(4, 32, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        csa2.csa2_quantize_fp4(x, 16, codes, scales)

@@ -1,0 +1,333 @@
+"""GPU parity, stage by stage, at sizes the oracle finishes in seconds.
+
+Every case feeds the HIP path and the oracle the same seeded inputs; where a
+stage consumes an upstream result, the GPU stage receives the oracle's
+result (never the other way round), so each stage is compared on its own.
+Sizes span several tiles and ragged tails; edge cases cover empty rows,
+n_vis below K, scale ties, subnormal scales and invalid ids.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import check_attention, check_selection
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(512)
+
+
+@pytest.fixture(scope="module")
+def csa2():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp4_compressed_sparse_e2m1_amd as m
+    m.load()
+    return m
+
+
+def dev(x, dtype=None):
+    t = torch.as_tensor(x)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.contiguous().cuda()
+
+
+def build_cache(csa2, lat_list, ik_list, cap):
+    """Quantise per-sequence fp32 rows into a fresh cache with the GPU kernel;
+    returns the cache and the oracle's codes for the same rows."""
+    S = len(lat_list)
+    cache = csa2.Cache(S, cap)
+    ora = []
+    for s, (lat, ik) in enumerate(zip(lat_list, ik_list)):
+        n = lat.shape[0]
+        dst = torch.arange(n, dtype=torch.int64, device="cuda") + s * cap
+        csa2.csa2_quantize_fp4(dev(lat), 16, cache.kv_codes, cache.kv_scales, dst_rows=dst)
+        csa2.csa2_quantize_fp4(dev(ik), 32, cache.ik_codes, cache.ik_scales, dst_rows=dst)
+        kvc, kvs = oracle.quantize(lat, 16)
+        ikc, iks = oracle.quantize(ik, 32)
+        ora.append((kvc, kvs, ikc, iks))
+    torch.cuda.synchronize()
+    return cache, ora
+
+
+# ---------------------------------------------------------------- S1 codec
+@pytest.mark.parametrize("dim,group", [(512, 16), (128, 32)])
+def test_quantize_bit_exact_random_and_edges(csa2, dim, group):
+    x = W.rms_rows(997, dim, seed=100 + dim).numpy()
+    x[1] *= 1e-3
+    x[2] *= 3e-5                      # subnormal scales
+    x[3] = 0.0                        # zero groups
+    x[4] *= 60.0
+    x[5, :group] = -1e-6              # scale underflow, negative zeros -> 0x8
+    x[6, 0] = -0.0
+    # a group fixing the scale at 0.5 with every E2M1 midpoint in it
+    x[7, :] = 0.0
+    x[7, 0] = 3.0
+    for i, t in enumerate([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]):
+        x[7, 1 + i] = 0.5 * t
+        if group > 8 + i:
+            x[7, 8 + i] = -0.5 * t
+    # scale ties: amax/6 halfway between two E4M3 values
+    x[8, :group] = 0.0
+    x[8, 0] = 6 * (0.5 + 0.5625) / 2
+    n = x.shape[0]
+    codes = torch.zeros((n, dim // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((n, dim // group), dtype=torch.uint8, device="cuda")
+    csa2.csa2_quantize_fp4(dev(x), group, codes, scales)
+    rc, rs = oracle.quantize(x, group)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_scatter_rows(csa2):
+    x = W.rms_rows(33, 512, seed=7).numpy()
+    dst = np.random.default_rng(0).choice(200, size=33, replace=False).astype(np.int64)
+    codes = torch.zeros((200, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((200, 32), dtype=torch.uint8, device="cuda")
+    csa2.csa2_quantize_fp4(dev(x), 16, codes, scales, dst_rows=dev(dst))
+    rc, rs = oracle.quantize(x, 16)
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    np.testing.assert_array_equal(c[dst], rc)
+    np.testing.assert_array_equal(s[dst], rs)
+    untouched = np.setdiff1d(np.arange(200), dst)
+    assert not c[untouched].any() and not s[untouched].any()
+
+
+# ------------------------------------------------------------- S2-S4 index
+def make_index_case(csa2, n_list, cap, seed, k_rows=None):
+    lat = [W.rms_rows(n, 512, seed=seed + 10 * i).numpy() for i, n in enumerate(n_list)]
+    ik = [W.rms_rows(n, 128, seed=seed + 10 * i + 1).numpy() for i, n in enumerate(n_list)]
+    cache, ora = build_cache(csa2, lat, ik, cap)
+    return cache, ora
+
+
+def run_full(csa2, cache, qidx, w, row_seq, row_nvis, max_nvis, k_blk, k_pos):
+    R = len(row_seq)
+    pool = torch.full((R, max(k_blk, 1)), -7, dtype=torch.int32, device="cuda")
+    npool = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    topk = torch.full((R, k_pos), -7, dtype=torch.int32, device="cuda")
+    ntopk = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(csa2.CSA2_OP_INDEX_FULL, R, max_nvis, k_blk, k_pos)
+    csa2.csa2_index_full(cache, qidx, w, dev(row_seq, torch.int32), dev(row_nvis, torch.int32),
+                         max_nvis, k_blk, k_pos, pool if k_blk else None, npool if k_blk else None,
+                         topk, ntopk, ws)
+    torch.cuda.synchronize()
+    return pool.cpu().numpy(), npool.cpu().numpy(), topk.cpu().numpy(), ntopk.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["decode_small", "ragged", "multilevel"])
+def test_index_full_block_mode(csa2, case):
+    if case == "decode_small":        # the tiny-decode shape: 4,096 entries, 64 blocks -> 512
+        n_list, rows, k_blk, k_pos = [4096], [(0, 4096)], 64, 512
+    elif case == "ragged":            # several sequences, ragged tails, empty and tiny rows
+        n_list = [5003, 77, 2000]
+        rows = [(0, 5003), (1, 77), (2, 1999), (0, 4096), (2, 0), (0, 9), (5, 100)]
+        k_blk, k_pos = 100, 64
+    else:                             # >16,384 blocks: two selection levels
+        n_list, rows, k_blk, k_pos = [140001], [(0, 140001), (0, 131072)], 2048, 512
+    cap = max(n_list) + 3
+    seeds = {"decode_small": 101, "ragged": 202, "multilevel": 303}
+    cache, ora = make_index_case(csa2, n_list, cap, seed=seeds[case])
+    R = len(rows)
+    qidx = W.bf16_normal((R, 8, 128), seed=5)
+    w = W.uniform01((R, 8), seed=6)
+    row_seq = [s for s, _ in rows]
+    row_nvis = [n for _, n in rows]
+    max_nvis = max(row_nvis)
+    pool, npool, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), row_seq, row_nvis,
+                                        max_nvis, k_blk, k_pos)
+    qb = W.bf16_bits(qidx)
+    wn = w.numpy()
+    for r, (s, nv) in enumerate(rows):
+        if s >= len(n_list):          # out-of-range sequence id -> empty row
+            assert npool[r] == 0 and ntopk[r] == 0
+            assert np.all(topk[r] == -1) and np.all(pool[r] == -1)
+            continue
+        _, _, ikc, iks = ora[s]
+        ref = oracle.full_layer_select(qb[r], wn[r], ikc, iks, nv, k_blk, k_pos)
+        bs = ref["block_scores"]
+        check_selection(pool[r], npool[r], np.pad(ref["pool"], (0, k_blk - len(ref["pool"])),
+                        constant_values=-1), len(ref["pool"]), lambda b: bs[b], "pool")
+        if np.array_equal(pool[r][:npool[r]], ref["pool"]):
+            sc = dict(zip(ref["cand"].tolist(), ref["cand_scores"].tolist()))
+            check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], "topk")
+
+
+@pytest.mark.parametrize("n_vis_rows", [[4096, 1000, 1], [20000, 16385, 300]])
+def test_index_full_flat_mode(csa2, n_vis_rows):
+    n = max(n_vis_rows)
+    cache, ora = make_index_case(csa2, [n], n, seed=17)
+    R = len(n_vis_rows)
+    qidx = W.bf16_normal((R, 8, 128), seed=8)
+    w = W.uniform01((R, 8), seed=9)
+    _, _, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [0] * R, n_vis_rows, n, 0, 512)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    _, _, ikc, iks = ora[0]
+    for r, nv in enumerate(n_vis_rows):
+        ref = oracle.full_layer_select(qb[r], wn[r], ikc, iks, nv, 0, 512)
+        sc = ref["entry_scores"]
+        check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], "flat")
+
+
+def test_index_reindex_on_oracle_pool(csa2):
+    n_list = [9000, 3001]
+    cache, ora = make_index_case(csa2, n_list, 9000, seed=23)
+    rows = [(0, 9000), (1, 3001), (0, 8191), (1, 5)]
+    R, k_blk, k_pos = len(rows), 300, 128
+    q_full = W.bf16_normal((R, 8, 128), seed=31)
+    w_full = W.uniform01((R, 8), seed=32)
+    q_re = W.bf16_normal((R, 8, 128), seed=33)
+    w_re = W.uniform01((R, 8), seed=34)
+    pools = np.full((R, k_blk), -1, np.int32)
+    npools = np.zeros(R, np.int32)
+    refs = []
+    for r, (s, nv) in enumerate(rows):
+        _, _, ikc, iks = ora[s]
+        f = oracle.full_layer_select(W.bf16_bits(q_full)[r], w_full.numpy()[r], ikc, iks, nv, k_blk, k_pos)
+        pools[r, :len(f["pool"])] = f["pool"]
+        npools[r] = len(f["pool"])
+        refs.append(oracle.reindex_select(W.bf16_bits(q_re)[r], w_re.numpy()[r], ikc, iks, nv,
+                                          f["pool"], k_pos))
+    topk = torch.full((R, k_pos), -7, dtype=torch.int32, device="cuda")
+    ntopk = torch.zeros(R, dtype=torch.int32, device="cuda")
+    max_nvis = max(n for _, n in rows)
+    ws = csa2.workspace(csa2.CSA2_OP_INDEX_REINDEX, R, max_nvis, k_blk, k_pos)
+    csa2.csa2_index_reindex(cache, dev(q_re), dev(w_re), dev([s for s, _ in rows], torch.int32),
+                            dev([n for _, n in rows], torch.int32), max_nvis, dev(pools), dev(npools),
+                            k_blk, k_pos, topk, ntopk, ws)
+    torch.cuda.synchronize()
+    topk, ntopk = topk.cpu().numpy(), ntopk.cpu().numpy()
+    for r in range(R):
+        sc = dict(zip(refs[r]["cand"].tolist(), refs[r]["cand_scores"].tolist()))
+        check_selection(topk[r], ntopk[r], refs[r]["topk"], refs[r]["n_topk"], lambda j: sc[j], "reindex")
+    # flat reindex (no pool): every visible entry is a candidate
+    ws2 = csa2.workspace(csa2.CSA2_OP_INDEX_REINDEX, R, max_nvis, 0, k_pos)
+    topk_t = torch.full((R, k_pos), -7, dtype=torch.int32, device="cuda")
+    ntopk_t = torch.zeros(R, dtype=torch.int32, device="cuda")
+    csa2.csa2_index_reindex(cache, dev(q_re), dev(w_re), dev([s for s, _ in rows], torch.int32),
+                            dev([n for _, n in rows], torch.int32), max_nvis, None, None, 0, k_pos,
+                            topk_t, ntopk_t, ws2)
+    torch.cuda.synchronize()
+    for r, (s, nv) in enumerate(rows):
+        _, _, ikc, iks = ora[s]
+        ref = oracle.reindex_select(W.bf16_bits(q_re)[r], w_re.numpy()[r], ikc, iks, nv, None, k_pos)
+        sc = ref["cand_scores"]
+        check_selection(topk_t.cpu().numpy()[r], ntopk_t.cpu().numpy()[r], ref["topk"], ref["n_topk"],
+                        lambda j: sc[j], "reindex-flat")
+
+
+# ------------------------------------------------------------ S5-S6 attention
+def attn_case(csa2, H, n_vis_list, topk_rows, swa_ends, seed=0, swa_len=200, window=128):
+    S = len(n_vis_list)
+    cap = max(n_vis_list)
+    lat = [W.rms_rows(n, 512, seed=seed + i).numpy() for i, n in enumerate(n_vis_list)]
+    ik = [np.zeros((n, 128), np.float32) for n in n_vis_list]
+    cache, ora = build_cache(csa2, lat, ik, cap)
+    swa = W.swa_rows_e4m3(S * swa_len, 512, seed=seed + 99).reshape(S, swa_len, 512)
+    R = len(topk_rows)
+    q = W.bf16_normal((R, H, 512), seed=seed + 7)
+    k_pos = max(len(t) for t, _ in topk_rows)
+    topk = np.full((R, k_pos), -1, np.int32)
+    ntopk = np.zeros(R, np.int32)
+    row_seq = np.zeros(R, np.int32)
+    for r, (ids, s) in enumerate(topk_rows):
+        topk[r, :len(ids)] = ids
+        ntopk[r] = len(ids)
+        row_seq[r] = s
+    return dict(cache=cache, ora=ora, swa=swa, q=q, topk=topk, ntopk=ntopk, row_seq=row_seq,
+                swa_end=np.asarray(swa_ends, np.int32), window=window, H=H)
+
+
+def oracle_attn(c, r):
+    s = int(c["row_seq"][r])
+    kvc, kvs, _, _ = c["ora"][s]
+    end = int(min(max(c["swa_end"][r], 0), c["swa"].shape[1]))
+    rows = c["swa"][s, max(0, end - c["window"]):end].numpy()
+    return oracle.attend_row(W.bf16_bits(c["q"][r]), kvc, kvs, c["topk"][r][:c["ntopk"][r]], rows, SCALE)
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_sparse_attn_global_fused_and_merge(csa2, H):
+    rng = np.random.default_rng(H)
+    nv = [3000, 700]
+    rows = [(np.sort(rng.choice(3000, 512, replace=False)), 0),      # full Top-512
+            (np.sort(rng.choice(700, 300, replace=False)), 1),       # ragged count
+            (np.array([], np.int64), 0),                             # no global keys
+            (np.sort(rng.choice(3000, 45, replace=False)), 0),
+            (np.array([5, -1, 17, 699, -1]), 1)]                     # invalid ids skipped
+    c = attn_case(csa2, H, nv, rows, swa_ends=[200, 128, 60, 0, 3], seed=H)
+    R = len(rows)
+    cache = c["cache"]
+    q = dev(c["q"])
+    row_seq = dev(c["row_seq"])
+    topk = dev(c["topk"])
+    ntopk = dev(c["ntopk"])
+    swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), c["window"])
+    refs = [oracle_attn(c, r) for r in range(R)]      # the oracle skips -1 ids as well
+    # global branch only
+    o = torch.empty((R, H, 512), device="cuda")
+    lse = torch.empty((R, H), device="cuda")
+    csa2.csa2_sparse_attn(cache, q, row_seq, topk, ntopk, SCALE, o, lse)
+    torch.cuda.synchronize()
+    check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o_g"] for x in refs]),
+                    np.stack([x["lse_g"] for x in refs]), "global")
+    # then the SWA branch merged onto it
+    csa2.csa2_swa_merge(q, row_seq, swa, SCALE, o, lse)
+    torch.cuda.synchronize()
+    check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o"] for x in refs]),
+                    np.stack([x["lse"] for x in refs]), "merged")
+    # fused: both branches in one softmax
+    o2 = torch.empty_like(o)
+    lse2 = torch.empty_like(lse)
+    csa2.csa2_sparse_attn(cache, q, row_seq, topk, ntopk, SCALE, o2, lse2, swa=swa)
+    torch.cuda.synchronize()
+    check_attention(o2.cpu().numpy(), lse2.cpu().numpy(), np.stack([x["o"] for x in refs]),
+                    np.stack([x["lse"] for x in refs]), "fused")
+
+
+def test_attention_empty_everything(csa2):
+    c = attn_case(csa2, 16, [100], [(np.array([], np.int64), 0)], swa_ends=[0], seed=3)
+    o = torch.full((1, 16, 512), 5.0, device="cuda")
+    lse = torch.zeros((1, 16), device="cuda")
+    swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), 128)
+    csa2.csa2_sparse_attn(c["cache"], dev(c["q"]), dev(c["row_seq"]), dev(c["topk"]),
+                          dev(c["ntopk"]), SCALE, o, lse, swa=swa)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# ------------------------------------------------------------- one layer e2e
+def test_tiny_full_decode_end_to_end(csa2):
+    """The tiny Full-mode decode (batch 1, 4,096 entries, 64 blocks -> 512,
+    16 heads, SWA 128): quantise, index, attend + merge, all on the GPU,
+    compared with the oracle pipeline on the same fp32 inputs."""
+    wl = W.WORKLOADS[0]
+    T = wl.ctx
+    lat = W.rms_rows(T, 512, seed=W.seed_for(wl.seed, W.T_LATENT)).numpy()
+    ik = W.rms_rows(T, 128, seed=W.seed_for(wl.seed, W.T_IKEY)).numpy()
+    cache, ora = build_cache(csa2, [lat], [ik], T)
+    kvc, kvs, ikc, iks = ora[0]
+    np.testing.assert_array_equal(cache.ik_codes[0].cpu().numpy(), ikc)
+    np.testing.assert_array_equal(cache.kv_scales[0].cpu().numpy(), kvs)
+    qidx = W.bf16_normal((1, 8, 128), seed=W.seed_for(wl.seed, W.T_QIDX))
+    w = W.uniform01((1, 8), seed=W.seed_for(wl.seed, W.T_W))
+    q = W.bf16_normal((1, wl.heads, 512), seed=W.seed_for(wl.seed, W.T_Q))
+    swa = W.swa_rows_e4m3(wl.swa, 512, seed=W.seed_for(wl.seed, W.T_SWA)).reshape(1, wl.swa, 512)
+    pool, npool, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [0], [T], T, wl.k_blk, wl.k_pos)
+    ref = oracle.full_layer_select(W.bf16_bits(qidx)[0], w.numpy()[0], ikc, iks, T, wl.k_blk, wl.k_pos)
+    bs = ref["block_scores"]
+    check_selection(pool[0], npool[0], ref["pool"], len(ref["pool"]), lambda b: bs[b], "pool")
+    assert ntopk[0] == 512
+    o = torch.empty((1, wl.heads, 512), device="cuda")
+    lse = torch.empty((1, wl.heads), device="cuda")
+    sw = csa2.Swa(dev(swa), dev(np.array([wl.swa], np.int32)), wl.swa)
+    csa2.csa2_sparse_attn(cache, dev(q), dev(np.array([0], np.int32)), dev(topk), dev(ntopk),
+                          SCALE, o, lse, swa=sw)
+    torch.cuda.synchronize()
+    r = oracle.attend_row(W.bf16_bits(q)[0], kvc, kvs, ref["topk"], swa[0].numpy(), SCALE)
+    check_attention(o.cpu().numpy()[0], lse.cpu().numpy()[0], r["o"], r["lse"], "tiny decode")
