@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 hot path on one MI355X.
+
+A step is one decode step of the 1M-context stack: batch 8, 1,048,576 visible
+entries per sequence, 20 CSA2 layers (1 Full, 4 Reindex, 15 Reuse), each
+with its own 16-head query and its own 128-row FP8 SWA window
+(P3 "레이어 40개 가운데 4개만 전역 캐시를 만듭니다"; P1 "무엇과 다른가").
+  Full    : append the step's new entry (FP4 quantise, both planes), scan all
+            1M entries, keep 2,048 blocks of 8, re-score the pool, Top-512,
+            sparse attention with the SWA branch in the same softmax;
+  Reindex : re-score the Full layer's pool with its own indexer query, Top-512,
+            attention + SWA;
+  Reuse   : attention + SWA over the last Reindex layer's Top-512.
+Inputs are seeded synthetic tensors already resident in HBM; the cache
+(8 x 1M entries x 356 B) is built before timing.
+
+Output: one JSON line.  value = query tokens per second per CSA2 layer
+(= batch x layers / step time); roofline = the Full-layer scan kernel,
+timed with HIP events on the stream it runs on; cpu_baseline = the oracle
+on a bounded sample of the same step.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+IK_BYTES = 68                  # indexer key bytes per entry (64 codes + 4 scales)
+SCALE = 1.0 / math.sqrt(512)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=4,
+                    help="query rows of the step the oracle runs for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ctx", type=int, default=None, help="override the context (testing only)")
+    return ap.parse_args()
+
+
+def build(ctx_override=None):
+    import torch
+
+    import fp4_compressed_sparse_e2m1_amd as csa2
+    import workloads as W
+
+    wl = W.WORKLOADS[3]
+    B, T, H = wl.batch, ctx_override or wl.ctx, wl.heads
+    dev = "cuda"
+    seed = wl.seed
+    cache = csa2.Cache(B, T, device=dev)
+    # bulk build of entries 0 .. T-2 (untimed); entry T-1 is the step's append
+    for s in range(B):
+        dst = torch.arange(T - 1, dtype=torch.int64, device=dev) + s * T
+        lat = W.rms_rows(T - 1, 512, W.seed_for(seed, W.T_LATENT, 0, s), device=dev)
+        csa2.csa2_quantize_fp4(lat, 16, cache.kv_codes, cache.kv_scales, dst_rows=dst)
+        del lat
+        ik = W.rms_rows(T - 1, 128, W.seed_for(seed, W.T_IKEY, 0, s), device=dev)
+        csa2.csa2_quantize_fp4(ik, 32, cache.ik_codes, cache.ik_scales, dst_rows=dst)
+        del ik, dst
+    torch.cuda.synchronize()
+    L = len(wl.layers)
+    new_lat = W.rms_rows(B, 512, W.seed_for(seed, W.T_LATENT, 0, 1 << 20), device=dev)
+    new_ik = W.rms_rows(B, 128, W.seed_for(seed, W.T_IKEY, 0, 1 << 20), device=dev)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    ctx = dict(
+        csa2=csa2, wl=wl, B=B, T=T, H=H, L=L, cache=cache, new_lat=new_lat, new_ik=new_ik,
+        new_dst=torch.arange(B, dtype=torch.int64, device=dev) * T + (T - 1),
+        row_seq=i32(list(range(B))), row_nvis=i32([T] * B),
+        q=[W.bf16_normal((B, H, 512), W.seed_for(seed, W.T_Q, l), device=dev) for l in range(L)],
+        q_idx=[W.bf16_normal((B, 8, 128), W.seed_for(seed, W.T_QIDX, l), device=dev) for l in range(L)],
+        w=[W.uniform01((B, 8), W.seed_for(seed, W.T_W, l), device=dev) for l in range(L)],
+        swa=[csa2.Swa(W.swa_rows_e4m3(B * wl.swa, 512, W.seed_for(seed, W.T_SWA, l), device=dev)
+                      .reshape(B, wl.swa, 512), i32([wl.swa] * B), wl.swa) for l in range(L)],
+        block_keys=csa2.block_keys_buffer(B, T),
+        pool=torch.empty((B, wl.k_blk), dtype=torch.int32, device=dev),
+        n_pool=torch.empty(B, dtype=torch.int32, device=dev),
+        topk=[torch.empty((B, wl.k_pos), dtype=torch.int32, device=dev) for _ in range(L)],
+        n_topk=[torch.empty(B, dtype=torch.int32, device=dev) for _ in range(L)],
+        ws_pool=csa2.workspace(csa2.CSA2_OP_INDEX_POOL, B, T, wl.k_blk, wl.k_pos),
+        ws_re=csa2.workspace(csa2.CSA2_OP_INDEX_REINDEX, B, T, wl.k_blk, wl.k_pos),
+        o=torch.empty((B, H, 512), dtype=torch.float32, device=dev),
+        lse=torch.empty((B, H), dtype=torch.float32, device=dev),
+    )
+    torch.cuda.synchronize()
+    return ctx
+
+
+def step(c, ev=None):
+    """One decode step of the 20-layer stack.  ev: optional list of event
+    pairs to record (scan start/end, then one boundary after every layer)."""
+    csa2, wl, T = c["csa2"], c["wl"], c["T"]
+    cache, seqs, nvis = c["cache"], c["row_seq"], c["row_nvis"]
+    src = None
+    for l, mode in enumerate(wl.layers):
+        if mode == "full":
+            csa2.csa2_quantize_fp4(c["new_lat"], 16, cache.kv_codes, cache.kv_scales, dst_rows=c["new_dst"])
+            csa2.csa2_quantize_fp4(c["new_ik"], 32, cache.ik_codes, cache.ik_scales, dst_rows=c["new_dst"])
+            if ev is not None:
+                ev["scan0"].record()
+            csa2.csa2_index_scan(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["block_keys"])
+            if ev is not None:
+                ev["scan1"].record()
+            csa2.csa2_index_pool(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["block_keys"],
+                                 wl.k_blk, wl.k_pos, c["pool"], c["n_pool"], c["topk"][l],
+                                 c["n_topk"][l], c["ws_pool"])
+            src = l
+        elif mode == "reindex":
+            csa2.csa2_index_reindex(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["pool"],
+                                    c["n_pool"], wl.k_blk, wl.k_pos, c["topk"][l], c["n_topk"][l],
+                                    c["ws_re"])
+            src = l
+        csa2.csa2_sparse_attn(cache, c["q"][l], seqs, c["topk"][src], c["n_topk"][src], SCALE,
+                              c["o"], c["lse"], swa=c["swa"][l])
+        if ev is not None:
+            ev["layer"][l].record()
+
+
+def run_gpu(c, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        step(c)
+    torch.cuda.synchronize()
+    L = c["L"]
+    evs = [dict(scan0=torch.cuda.Event(enable_timing=True), scan1=torch.cuda.Event(enable_timing=True),
+                start=torch.cuda.Event(enable_timing=True),
+                layer=[torch.cuda.Event(enable_timing=True) for _ in range(L)]) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        evs[k]["start"].record()
+        step(c, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = sum(e["scan0"].elapsed_time(e["scan1"]) for e in evs) / steps
+    per_layer = [0.0] * L
+    for e in evs:
+        prev = e["start"]
+        for l in range(L):
+            per_layer[l] += prev.elapsed_time(e["layer"][l]) / steps
+            prev = e["layer"][l]
+    return wall, scan_ms, per_layer
+
+
+def cpu_baseline(c, rows):
+    """The oracle, as it stands, on `rows` query rows of the same step (all 20
+    layers, full 1M context), one host thread per row.  The oracle builds its
+    own FP4 cache of those rows' sequences from the same fp32 generator before
+    timing; the timed part is what the GPU step does: append, scan, pool,
+    Top-512, 4 re-indexes and 20 attentions with SWA."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+
+    wl, T, B = c["wl"], c["T"], c["B"]
+    rows = max(1, min(rows, B))
+    seed = wl.seed
+    prep = []
+    for s in range(rows):
+        ik = W.rms_rows(T - 1, 128, W.seed_for(seed, W.T_IKEY, 0, s), device="cuda").cpu().numpy()
+        ik = np.concatenate([ik, c["new_ik"][s:s + 1].cpu().numpy()])
+        prep.append(ik)
+
+    def quantize_seq(s):
+        return oracle.quantize(prep[s], oracle.IK_GROUP)
+
+    planes = oracle.parallel_map(quantize_seq, list(range(rows)), rows)
+    del prep
+    lat_rows = {}
+    swa = [c["swa"][l].kv.cpu().numpy() for l in range(c["L"])]
+    q = [W.bf16_bits(c["q"][l]) for l in range(c["L"])]
+    qi = [W.bf16_bits(c["q_idx"][l]) for l in range(c["L"])]
+    wv = [c["w"][l].cpu().numpy() for l in range(c["L"])]
+
+    def full_step(s):
+        ikc, iks = planes[s]
+        sel = None
+        out = []
+        for l, mode in enumerate(wl.layers):
+            if mode == "full":
+                f = oracle.full_layer_select(qi[l][s], wv[l][s], ikc, iks, T, wl.k_blk, wl.k_pos)
+                pool, sel = f["pool"], f["topk"]
+            elif mode == "reindex":
+                sel = oracle.reindex_select(qi[l][s], wv[l][s], ikc, iks, T, pool, wl.k_pos)["topk"]
+            ids = sel[sel >= 0]
+            kvc, kvs = lat_rows[s]
+            kmap = {int(j): i for i, j in enumerate(lat_rows[(s, "ids")])}
+            loc = np.array([kmap[int(j)] for j in ids], np.int32)
+            out.append(oracle.attend_row(q[l][s], kvc, kvs, loc, swa[l][s], SCALE)["o"])
+        return out
+
+    # the main latents of every entry the oracle will gather (from the same
+    # generator), quantised by the oracle itself before timing
+    for s in range(rows):
+        ikc, iks = planes[s]
+        ids = set()
+        f = oracle.full_layer_select(qi[0][s], wv[0][s], ikc, iks, T, wl.k_blk, wl.k_pos)
+        ids.update(f["topk"][f["topk"] >= 0].tolist())
+        for l, mode in enumerate(wl.layers):
+            if mode == "reindex":
+                r = oracle.reindex_select(qi[l][s], wv[l][s], ikc, iks, T, f["pool"], wl.k_pos)
+                ids.update(r["topk"][r["topk"] >= 0].tolist())
+        ids = np.array(sorted(ids), np.int64)
+        lat = W.rms_rows(T - 1, 512, W.seed_for(seed, W.T_LATENT, 0, s), device="cuda")
+        lat = torch.cat([lat, c["new_lat"][s:s + 1]])
+        lat_rows[s] = oracle.quantize(lat[torch.from_numpy(ids).cuda()].cpu().numpy(), oracle.KV_GROUP)
+        lat_rows[(s, "ids")] = ids
+        del lat
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    oracle.parallel_map(full_step, list(range(rows)), rows)
+    dt = time.perf_counter() - t0
+    return {"value": rows * c["L"] / dt, "unit": "query-tokens/s per CSA2 layer", "cores": rows,
+            "kind": "oracle",
+            "sample": f"{rows} of the {B} query rows of the 1M-context decode step, all {c['L']} layers "
+                      f"(scan of {T} entries, pool, Top-512, 4 re-indexes, 20 attentions with SWA), "
+                      f"one host thread per row; {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(every step of the CSA2 path is independent per sequence, so N GPUs would each run "
+              f"their own share of the batch).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    import fp4_compressed_sparse_e2m1_amd as csa2
+    csa2.load()
+    t_build = time.perf_counter()
+    c = build(args.ctx)
+    t_build = time.perf_counter() - t_build
+    wall, scan_ms, per_layer = run_gpu(c, args.steps, args.warmup)
+    B, T, L = c["B"], c["T"], c["L"]
+    ms_step = wall * 1e3 / args.steps
+    value = B * L / (wall / args.steps)
+    scan_bytes = IK_BYTES * T * B
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    modes = c["wl"].layers
+    mode_us = {m: 1e3 * sum(t for t, mm in zip(per_layer, modes) if mm == m) /
+               max(1, sum(1 for mm in modes if mm == m)) for m in ("full", "reindex", "reuse")}
+    line = {
+        "metric": "decode query-tokens/s per CSA2 layer at 1M ctx; HBM GB/s % of peak",
+        "value": round(value, 1),
+        "unit": "query-tokens/s per CSA2 layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": c["wl"].name, "batch": B, "context_entries": T, "layers": L,
+                   "layer_modes": {"full": 1, "reindex": 4, "reuse": 15}, "heads": c["H"],
+                   "k_blocks": c["wl"].k_blk, "k_pos": c["wl"].k_pos, "swa": c["wl"].swa,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "score_kernel<block max> (csa2_index_scan)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(scan_ms * 1e3, 2)},
+        "per_layer_us": {k: round(v, 2) for k, v in mode_us.items()},
+        "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
+        "build_s": round(t_build, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

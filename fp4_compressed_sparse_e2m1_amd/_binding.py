@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 CSA2_OK = 0
 CSA2_OP_INDEX_FULL = 1
 CSA2_OP_INDEX_REINDEX = 2
+CSA2_OP_INDEX_POOL = 3
 
 _lib = None
 _lock = threading.Lock()
@@ -53,12 +54,16 @@ def load():
             _build.build()
         lib = ctypes.CDLL(LIB_PATH)
         P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        lib.csa2_quantize_fp4.argtypes = [P, i64, i32, i32, P, P, P, P]
+        lib.csa2_quantize_fp4.argtypes = [P, i64, i32, i32, P, P, P, i64, P]
         lib.csa2_quantize_fp4.restype = ctypes.c_int
         lib.csa2_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         lib.csa2_workspace_size.restype = sz
         lib.csa2_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         lib.csa2_index_full.restype = ctypes.c_int
+        lib.csa2_index_scan.argtypes = [P, P, P, P, P, i32, i32, P, P]
+        lib.csa2_index_scan.restype = ctypes.c_int
+        lib.csa2_index_pool.argtypes = [P, P, P, P, P, i32, i32, P, i32, i32, P, P, P, P, P, sz, P]
+        lib.csa2_index_pool.restype = ctypes.c_int
         lib.csa2_index_reindex.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, P, P, P, sz, P]
         lib.csa2_index_reindex.restype = ctypes.c_int
         lib.csa2_sparse_attn.argtypes = [P, P, i32, P, i32, P, P, i32, ctypes.c_float, P, P, P, P]
@@ -171,7 +176,7 @@ def csa2_quantize_fp4(x, group, codes, scales, dst_rows=None, stream=None):
     st = lib.csa2_quantize_fp4(_ptr(x, torch.float32, "x"), n, dim, group,
                                _ptr(dst_rows, torch.int64, "dst_rows", (n,), allow_none=True),
                                _ptr(codes, torch.uint8, "codes"), _ptr(scales, torch.uint8, "scales"),
-                               _stream(stream))
+                               rows, _stream(stream))
     _check("csa2_quantize_fp4", st)
 
 
@@ -188,6 +193,38 @@ def csa2_index_full(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, k_block
         _ptr(topk, torch.int32, "topk", (R, k_pos)), _ptr(n_topk, torch.int32, "n_topk", (R,)),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check("csa2_index_full", st)
+
+
+def block_keys_buffer(n_rows: int, max_nvis: int, device="cuda"):
+    """uint32 block-score keys [n_rows, max(1, ceil(max_nvis / 8))] (held as int32)."""
+    return torch.empty((n_rows, max(1, (max_nvis + 7) // 8)), dtype=torch.int32, device=device)
+
+
+def csa2_index_scan(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, block_keys, stream=None):
+    R = row_seq.shape[0]
+    cs = cache.struct()
+    st = load().csa2_index_scan(
+        ctypes.byref(cs), _ptr(q_idx, torch.bfloat16, "q_idx", (R, 8, 128)),
+        _ptr(w, torch.float32, "w", (R, 8)), _ptr(row_seq, torch.int32, "row_seq", (R,)),
+        _ptr(row_nvis, torch.int32, "row_nvis", (R,)), R, int(max_nvis),
+        _ptr(block_keys, torch.int32, "block_keys", (R, max(1, (max_nvis + 7) // 8))), _stream(stream))
+    _check("csa2_index_scan", st)
+
+
+def csa2_index_pool(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, block_keys, k_blocks, k_pos,
+                    pool_blocks, n_pool, topk, n_topk, workspace, stream=None):
+    R = row_seq.shape[0]
+    cs = cache.struct()
+    st = load().csa2_index_pool(
+        ctypes.byref(cs), _ptr(q_idx, torch.bfloat16, "q_idx", (R, 8, 128)),
+        _ptr(w, torch.float32, "w", (R, 8)), _ptr(row_seq, torch.int32, "row_seq", (R,)),
+        _ptr(row_nvis, torch.int32, "row_nvis", (R,)), R, int(max_nvis),
+        _ptr(block_keys, torch.int32, "block_keys", (R, max(1, (max_nvis + 7) // 8))),
+        int(k_blocks), int(k_pos), _ptr(pool_blocks, torch.int32, "pool_blocks", (R, k_blocks)),
+        _ptr(n_pool, torch.int32, "n_pool", (R,)), _ptr(topk, torch.int32, "topk", (R, k_pos)),
+        _ptr(n_topk, torch.int32, "n_topk", (R,)), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream))
+    _check("csa2_index_pool", st)
 
 
 def csa2_index_reindex(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, pool_blocks, n_pool,

@@ -55,10 +55,12 @@ Layout plan_workspace(int32_t op, int32_t rows, int32_t max_nvis, int32_t k_bloc
   size_t off = 0;
   size_t half = 0;
   if (k_blocks > 0) {
-    if (op == CSA2_OP_INDEX_FULL) {
+    if (op == CSA2_OP_INDEX_FULL || op == CSA2_OP_INDEX_POOL) {
       const int64_t nb = ((int64_t)max_nvis + 7) / 8;
-      L.keys_a = off;
-      off += round_up((size_t)rows * (size_t)(nb > 0 ? nb : 1) * 4);
+      if (op == CSA2_OP_INDEX_FULL) {
+        L.keys_a = off;
+        off += round_up((size_t)rows * (size_t)(nb > 0 ? nb : 1) * 4);
+      }
       half = select_scratch(rows, nb, k_blocks);
     }
     L.keys_b = off;
@@ -161,29 +163,20 @@ bool cache_ok(const csa2_cache *c, bool need_kv, bool need_ik) {
 }
 
 // Shared body of index_full / index_reindex.
-csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_idx, const float *w,
-                        const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
-                        int32_t max_nvis, const int32_t *pool_in, const int32_t *n_pool_in,
-                        int32_t k_blocks, int32_t k_pos, int32_t *pool_out, int32_t *n_pool_out,
-                        int32_t *topk, int32_t *n_topk, void *workspace, size_t workspace_bytes,
-                        void *stream_ptr) {
+// Host checks shared by every indexer entry point.
+csa2_status check_index_args(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                             const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                             int32_t max_nvis) {
   if (!cache_ok(cache, false, true)) return CSA2_E_INVALID_ARG;
-  if (!q_idx || !w || !row_seq || !row_nvis || !topk || !n_topk) return CSA2_E_INVALID_ARG;
-  if (n_rows < 1 || max_nvis < 0 || (int64_t)max_nvis > cache->cap || k_pos < 1 || k_blocks < 0)
-    return CSA2_E_INVALID_ARG;
+  if (!q_idx || !w || !row_seq || !row_nvis) return CSA2_E_INVALID_ARG;
+  if (n_rows < 1 || max_nvis < 0 || (int64_t)max_nvis > cache->cap) return CSA2_E_INVALID_ARG;
   if (!aligned(q_idx, 16) || !aligned(w, 4)) return CSA2_E_INVALID_ARG;
-  if (n_rows > kMaxGridY || k_pos > kMaxPos || k_blocks > kMaxBlocks ||
-      max_nvis > 0x7FFFFFF0)
-    return CSA2_E_UNSUPPORTED;
-  const bool pool_mode = k_blocks > 0;
-  if (op == CSA2_OP_INDEX_FULL && pool_mode && (!pool_out || !n_pool_out)) return CSA2_E_INVALID_ARG;
-  if (op == CSA2_OP_INDEX_REINDEX && pool_mode && (!pool_in || !n_pool_in)) return CSA2_E_INVALID_ARG;
-  const Layout L = plan_workspace(op, n_rows, max_nvis, k_blocks, k_pos);
-  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
-  if (prepare() != hipSuccess) return CSA2_E_HIP;
+  if (n_rows > kMaxGridY || max_nvis > 0x7FFFFFF0) return CSA2_E_UNSUPPORTED;
+  return CSA2_OK;
+}
 
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-  uint8_t *ws = static_cast<uint8_t *>(workspace);
+ScoreArgs score_args(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                     const int32_t *row_seq, const int32_t *row_nvis, int32_t max_nvis) {
   ScoreArgs sa = {};
   sa.ik_codes = cache->ik_codes;
   sa.ik_scales = cache->ik_scales;
@@ -194,6 +187,33 @@ csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_i
   sa.row_seq = row_seq;
   sa.row_nvis = row_nvis;
   sa.max_nvis = max_nvis;
+  return sa;
+}
+
+csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                        const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                        int32_t max_nvis, const uint32_t *ext_block_keys, const int32_t *pool_in,
+                        const int32_t *n_pool_in, int32_t k_blocks, int32_t k_pos,
+                        int32_t *pool_out, int32_t *n_pool_out, int32_t *topk, int32_t *n_topk,
+                        void *workspace, size_t workspace_bytes, void *stream_ptr) {
+  const csa2_status cs = check_index_args(cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis);
+  if (cs != CSA2_OK) return cs;
+  if (!topk || !n_topk || k_pos < 1 || k_blocks < 0) return CSA2_E_INVALID_ARG;
+  if (k_pos > kMaxPos || k_blocks > kMaxBlocks) return CSA2_E_UNSUPPORTED;
+  const bool pool_mode = k_blocks > 0;
+  if ((op == CSA2_OP_INDEX_FULL || op == CSA2_OP_INDEX_POOL) && pool_mode &&
+      (!pool_out || !n_pool_out))
+    return CSA2_E_INVALID_ARG;
+  if (op == CSA2_OP_INDEX_POOL && (!pool_mode || !ext_block_keys || !aligned(ext_block_keys, 4)))
+    return CSA2_E_INVALID_ARG;
+  if (op == CSA2_OP_INDEX_REINDEX && pool_mode && (!pool_in || !n_pool_in)) return CSA2_E_INVALID_ARG;
+  const Layout L = plan_workspace(op, n_rows, max_nvis, k_blocks, k_pos);
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
+  if (prepare() != hipSuccess) return CSA2_E_HIP;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  ScoreArgs sa = score_args(cache, q_idx, w, row_seq, row_nvis, max_nvis);
   hipError_t e = hipSuccess;
 
   if (!pool_mode) {
@@ -210,15 +230,20 @@ csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_i
 
   const int32_t *pool = pool_in;
   const int32_t *npool = n_pool_in;
-  if (op == CSA2_OP_INDEX_FULL) {
+  if (op == CSA2_OP_INDEX_FULL || op == CSA2_OP_INDEX_POOL) {
     // scan: block max of every visible entry's score, then the block Top-k
     const int64_t nb = ((int64_t)max_nvis + 7) / 8;
-    sa.keys_out = reinterpret_cast<uint32_t *>(ws + L.keys_a);
-    sa.out_stride = nb > 0 ? nb : 1;
-    e = launch_score(kScoreBlockMax, sa, n_rows, max_nvis, stream);
-    if (e != hipSuccess) return CSA2_E_HIP;
+    const int64_t nb_stride = nb > 0 ? nb : 1;
+    const uint32_t *bkeys = ext_block_keys;
+    if (op == CSA2_OP_INDEX_FULL) {
+      sa.keys_out = reinterpret_cast<uint32_t *>(ws + L.keys_a);
+      sa.out_stride = nb_stride;
+      e = launch_score(kScoreBlockMax, sa, n_rows, max_nvis, stream);
+      if (e != hipSuccess) return CSA2_E_HIP;
+      bkeys = sa.keys_out;
+    }
     SelectOut fin = {pool_out, n_pool_out, kMapId, nullptr, nullptr, 0};
-    e = run_select(sa.keys_out, sa.out_stride, kCountNvisBlocks, 0, nb, k_blocks, row_seq, row_nvis,
+    e = run_select(bkeys, nb_stride, kCountNvisBlocks, 0, nb, k_blocks, row_seq, row_nvis,
                    cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half, n_rows, stream);
     if (e != hipSuccess) return CSA2_E_HIP;
     pool = pool_out;
@@ -250,23 +275,24 @@ extern "C" {
 
 csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t group,
                               const int64_t *dst_rows, uint8_t *codes, uint8_t *scales,
-                              void *stream) {
-  if (n < 0) return CSA2_E_INVALID_ARG;
+                              int64_t plane_rows, void *stream) {
+  if (n < 0 || plane_rows < 0 || (!dst_rows && plane_rows < n)) return CSA2_E_INVALID_ARG;
   if (group != 16 && group != 32) return CSA2_E_UNSUPPORTED;
   if (dim < 32 || dim > 4096 || dim % group != 0) return CSA2_E_UNSUPPORTED;
   if (n == 0) return CSA2_OK;
   if (!x || !codes || !scales) return CSA2_E_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(codes, group == 16 ? 8 : 16)) return CSA2_E_INVALID_ARG;
   if (n > ((int64_t)1 << 40) / dim) return CSA2_E_UNSUPPORTED;
-  hipError_t e = launch_quantize(x, n, dim, group, dst_rows, codes, scales,
+  hipError_t e = launch_quantize(x, n, dim, group, dst_rows, codes, scales, plane_rows,
                                  reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
 }
 
 size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,
                            int32_t k_pos) {
-  if ((op != CSA2_OP_INDEX_FULL && op != CSA2_OP_INDEX_REINDEX) || n_rows < 1 || max_nvis < 0 ||
-      k_blocks < 0 || k_blocks > kMaxBlocks || k_pos < 1 || k_pos > kMaxPos)
+  if ((op != CSA2_OP_INDEX_FULL && op != CSA2_OP_INDEX_REINDEX && op != CSA2_OP_INDEX_POOL) ||
+      n_rows < 1 || max_nvis < 0 || k_blocks < 0 || k_blocks > kMaxBlocks || k_pos < 1 ||
+      k_pos > kMaxPos || (op == CSA2_OP_INDEX_POOL && k_blocks < 1))
     return 0;
   return plan_workspace(op, n_rows, max_nvis, k_blocks, k_pos).total;
 }
@@ -278,8 +304,35 @@ csa2_status csa2_index_full(const csa2_cache *cache, const uint16_t *q_idx, cons
                             int32_t *n_topk, void *workspace, size_t workspace_bytes,
                             void *stream) {
   return run_indexer(CSA2_OP_INDEX_FULL, cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis,
-                     nullptr, nullptr, k_blocks, k_pos, pool_blocks, n_pool, topk, n_topk,
+                     nullptr, nullptr, nullptr, k_blocks, k_pos, pool_blocks, n_pool, topk, n_topk,
                      workspace, workspace_bytes, stream);
+}
+
+csa2_status csa2_index_scan(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                            const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                            int32_t max_nvis, uint32_t *block_keys, void *stream) {
+  const csa2_status cs = check_index_args(cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis);
+  if (cs != CSA2_OK) return cs;
+  if (!block_keys || !aligned(block_keys, 4)) return CSA2_E_INVALID_ARG;
+  if (prepare() != hipSuccess) return CSA2_E_HIP;
+  ScoreArgs sa = score_args(cache, q_idx, w, row_seq, row_nvis, max_nvis);
+  const int64_t nb = ((int64_t)max_nvis + 7) / 8;
+  sa.keys_out = block_keys;
+  sa.out_stride = nb > 0 ? nb : 1;
+  hipError_t e = launch_score(kScoreBlockMax, sa, n_rows, max_nvis, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
+csa2_status csa2_index_pool(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                            const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                            int32_t max_nvis, const uint32_t *block_keys, int32_t k_blocks,
+                            int32_t k_pos, int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
+                            int32_t *n_topk, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  if (k_blocks < 1) return CSA2_E_INVALID_ARG;
+  return run_indexer(CSA2_OP_INDEX_POOL, cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis,
+                     block_keys, nullptr, nullptr, k_blocks, k_pos, pool_blocks, n_pool, topk,
+                     n_topk, workspace, workspace_bytes, stream);
 }
 
 csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
@@ -291,8 +344,8 @@ csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, c
   const int32_t kb = pool_blocks ? k_blocks : 0;
   if (pool_blocks && k_blocks < 1) return CSA2_E_INVALID_ARG;
   return run_indexer(CSA2_OP_INDEX_REINDEX, cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis,
-                     pool_blocks, n_pool, kb, k_pos, nullptr, nullptr, topk, n_topk, workspace,
-                     workspace_bytes, stream);
+                     nullptr, pool_blocks, n_pool, kb, k_pos, nullptr, nullptr, topk, n_topk,
+                     workspace, workspace_bytes, stream);
 }
 
 csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,

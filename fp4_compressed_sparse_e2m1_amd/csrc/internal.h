@@ -93,6 +93,6 @@ hipError_t prepare_attention();
 
 // ---------------------------------------------------------------- quantise
 hipError_t launch_quantize(const float *x, int64_t n, int dim, int group, const int64_t *dst_rows,
-                           uint8_t *codes, uint8_t *scales, hipStream_t stream);
+                           uint8_t *codes, uint8_t *scales, int64_t plane_rows, hipStream_t stream);
 
 }  // namespace csa2

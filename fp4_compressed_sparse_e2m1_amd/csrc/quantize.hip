@@ -48,12 +48,14 @@ __device__ __forceinline__ uint32_t e2m1_mag(float a, float s) {
 template <int G>
 __global__ void __launch_bounds__(256)
 quantize_kernel(const float *__restrict__ x, int64_t n, int dim, const int64_t *__restrict__ dst_rows,
-                uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+                uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, int64_t plane_rows) {
   const int ngroups = dim / G;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n * ngroups) return;
   const int64_t r = idx / ngroups;
   const int g = (int)(idx - r * ngroups);
+  const int64_t dst = dst_rows ? dst_rows[r] : r;
+  if (dst < 0 || dst >= plane_rows) return;
   const float4 *src = reinterpret_cast<const float4 *>(x + r * dim + (int64_t)g * G);
   float v[G];
 #pragma unroll
@@ -82,7 +84,6 @@ quantize_kernel(const float *__restrict__ x, int64_t n, int dim, const int64_t *
     }
     packed[w] = word;
   }
-  const int64_t dst = dst_rows ? dst_rows[r] : r;
   uint8_t *cdst = codes + dst * (dim / 2) + (int64_t)g * (G / 2);
   if constexpr (G == 16) {
     *reinterpret_cast<uint2 *>(cdst) = make_uint2(packed[0], packed[1]);
@@ -95,14 +96,14 @@ quantize_kernel(const float *__restrict__ x, int64_t n, int dim, const int64_t *
 }  // namespace
 
 hipError_t launch_quantize(const float *x, int64_t n, int dim, int group, const int64_t *dst_rows,
-                           uint8_t *codes, uint8_t *scales, hipStream_t stream) {
+                           uint8_t *codes, uint8_t *scales, int64_t plane_rows, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t total = n * (dim / group);
   const unsigned blocks = (unsigned)((total + 255) / 256);
   if (group == 16)
-    quantize_kernel<16><<<blocks, 256, 0, stream>>>(x, n, dim, dst_rows, codes, scales);
+    quantize_kernel<16><<<blocks, 256, 0, stream>>>(x, n, dim, dst_rows, codes, scales, plane_rows);
   else
-    quantize_kernel<32><<<blocks, 256, 0, stream>>>(x, n, dim, dst_rows, codes, scales);
+    quantize_kernel<32><<<blocks, 256, 0, stream>>>(x, n, dim, dst_rows, codes, scales, plane_rows);
   return hipGetLastError();
 }
 

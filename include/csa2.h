@@ -72,7 +72,7 @@ typedef enum {
 } csa2_status;
 
 /* Operation ids for csa2_workspace_size(). */
-enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_INDEX_REINDEX = 2 };
+enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_INDEX_REINDEX = 2, CSA2_OP_INDEX_POOL = 3 };
 
 /* Global (compressed) KV cache of one Full layer: four device planes, laid
  * out as in the header comment.  Entry j of sequence s lives at row
@@ -115,16 +115,21 @@ typedef struct {
  * when dst_rows is NULL:
  *   codes  + dst * (dim/2)       (dim/2 bytes)
  *   scales + dst * (dim/group)   (dim/group bytes).
+ * The planes hold plane_rows rows; rows whose dst lies outside
+ * [0, plane_rows) are skipped.
  * To append entry j of sequence s to a csa2_cache, use dst = s * cap + j with
- * (dim, group) = (512, 16) on kv_* and (128, 32) on ik_*.
- * Requires n >= 0, group in {16, 32}, dim % group == 0, 32 <= dim <= 4096. */
+ * (dim, group) = (512, 16) on kv_* and (128, 32) on ik_* and
+ * plane_rows = n_seq * cap.
+ * Requires n >= 0, group in {16, 32}, dim % group == 0, 32 <= dim <= 4096,
+ * plane_rows >= 0 (and plane_rows >= n when dst_rows is NULL). */
 csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t group,
                               const int64_t *dst_rows, uint8_t *codes, uint8_t *scales,
-                              void *stream);
+                              int64_t plane_rows, void *stream);
 
-/* Scratch bytes that csa2_index_full (op CSA2_OP_INDEX_FULL) or
- * csa2_index_reindex (op CSA2_OP_INDEX_REINDEX) needs for these sizes;
- * k_blocks = 0 selects flat mode.  Returns 0 for invalid arguments. */
+/* Scratch bytes that csa2_index_full (op CSA2_OP_INDEX_FULL),
+ * csa2_index_reindex (op CSA2_OP_INDEX_REINDEX) or csa2_index_pool (op
+ * CSA2_OP_INDEX_POOL) needs for these sizes; k_blocks = 0 selects flat mode
+ * (not valid for CSA2_OP_INDEX_POOL).  Returns 0 for invalid arguments. */
 size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,
                            int32_t k_pos);
 
@@ -156,6 +161,33 @@ csa2_status csa2_index_full(const csa2_cache *cache, const uint16_t *q_idx, cons
                             const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
                             int32_t max_nvis, int32_t k_blocks, int32_t k_pos,
                             int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
+                            int32_t *n_topk, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* S2 alone -- the scan stage of csa2_index_full in block mode, for callers
+ * that schedule or time the context-proportional scan separately.  For each
+ * row, writes the score of every visible block (as csa2_index_full defines
+ * it) to block_keys[r][b], b < ceil(n_vis / 8), as an order-preserving
+ * uint32 image of the fp32 score: key = bits ^ 0x80000000 for scores >= +0,
+ * key = ~bits for negative scores (a larger key means a larger score).
+ * block_keys: device uint32 [n_rows][ceil(max_nvis / 8)] (row stride
+ * ceil(max_nvis / 8), at least 1); slots past a row's block count are left
+ * untouched.  Same argument rules as csa2_index_full. */
+csa2_status csa2_index_scan(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                            const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                            int32_t max_nvis, uint32_t *block_keys, void *stream);
+
+/* S3 + S4 on a finished scan -- the remaining stages of csa2_index_full in
+ * block mode: block Top-k_blocks from block_keys (as written by
+ * csa2_index_scan for the same rows), the pool, its re-scoring with the same
+ * q_idx and w, and the Top-k_pos positions.  Outputs and limits as
+ * csa2_index_full with k_blocks >= 1; workspace sized with
+ * CSA2_OP_INDEX_POOL.  csa2_index_scan followed by csa2_index_pool gives the
+ * same results as csa2_index_full. */
+csa2_status csa2_index_pool(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                            const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                            int32_t max_nvis, const uint32_t *block_keys, int32_t k_blocks,
+                            int32_t k_pos, int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
                             int32_t *n_topk, void *workspace, size_t workspace_bytes,
                             void *stream);
 

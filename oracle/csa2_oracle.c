@@ -58,15 +58,26 @@ double oracle_e4m3_value(int byte)
     return s ? -v : v;
 }
 
+/* Values of the 127 finite non-negative E4M3FN codes and of the 8 E2M1
+ * magnitudes, filled once when the library is loaded (the same numbers
+ * oracle_e4m3_value and oracle_e2m1_value return). */
+static double g_e4m3_pos[0x7F];
+static double g_e2m1_pos[8];
+__attribute__((constructor)) static void fill_tables(void)
+{
+    for (int b = 0; b <= 0x7E; ++b) g_e4m3_pos[b] = oracle_e4m3_value(b);
+    for (int c = 0; c < 8; ++c) g_e2m1_pos[c] = oracle_e2m1_value(c);
+}
+
 /* Nearest non-negative E4M3FN value to v >= 0, ties to the even code
  * (mantissa LSB 0).  Exhaustive search over the 127 finite non-negative codes;
  * values above 448 therefore land on 448 (saturation). */
 static int encode_e4m3_nonneg(double v)
 {
     int best = 0;
-    double best_d = fabs(v - oracle_e4m3_value(0));
+    double best_d = fabs(v - g_e4m3_pos[0]);
     for (int b = 1; b <= 0x7E; ++b) {
-        double d = fabs(v - oracle_e4m3_value(b));
+        double d = fabs(v - g_e4m3_pos[b]);
         if (d < best_d || (d == best_d && (b & 1) == 0 && (best & 1) == 1)) {
             best = b;
             best_d = d;
@@ -79,9 +90,9 @@ static int encode_e4m3_nonneg(double v)
 static int encode_e2m1_mag(double y)
 {
     int best = 0;
-    double best_d = fabs(y - oracle_e2m1_value(0));
+    double best_d = fabs(y - g_e2m1_pos[0]);
     for (int c = 1; c <= 7; ++c) {
-        double d = fabs(y - oracle_e2m1_value(c));
+        double d = fabs(y - g_e2m1_pos[c]);
         if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
             best = c;
             best_d = d;

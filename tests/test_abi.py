@@ -28,7 +28,7 @@ def test_exports_every_declared_function():
     lib = csa2.load()
     names = declared_functions()
     assert {"csa2_quantize_fp4", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
-            "csa2_swa_merge"} <= set(names)
+            "csa2_swa_merge", "csa2_index_scan", "csa2_index_pool"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
 
@@ -58,13 +58,15 @@ def cache_struct(cap=100, n_seq=1, null_ik=False):
 def test_quantize_validation():
     lib = csa2.load()
     f = lib.csa2_quantize_fp4
-    assert f(FAKE, -1, 512, 16, None, FAKE, FAKE, None) == INVALID
-    assert f(FAKE, 4, 512, 8, None, FAKE, FAKE, None) == UNSUPPORTED
-    assert f(FAKE, 4, 520, 16, None, FAKE, FAKE, None) == UNSUPPORTED
-    assert f(FAKE, 4, 16, 16, None, FAKE, FAKE, None) == UNSUPPORTED
-    assert f(None, 4, 512, 16, None, FAKE, FAKE, None) == INVALID
-    assert f(FAKE + 4, 4, 512, 16, None, FAKE, FAKE, None) == INVALID     # misaligned x
-    assert f(FAKE, 0, 512, 16, None, None, None, None) == OK              # nothing to do
+    assert f(FAKE, -1, 512, 16, None, FAKE, FAKE, 4, None) == INVALID
+    assert f(FAKE, 4, 512, 8, None, FAKE, FAKE, 4, None) == UNSUPPORTED
+    assert f(FAKE, 4, 520, 16, None, FAKE, FAKE, 4, None) == UNSUPPORTED
+    assert f(FAKE, 4, 16, 16, None, FAKE, FAKE, 4, None) == UNSUPPORTED
+    assert f(None, 4, 512, 16, None, FAKE, FAKE, 4, None) == INVALID
+    assert f(FAKE + 4, 4, 512, 16, None, FAKE, FAKE, 4, None) == INVALID     # misaligned x
+    assert f(FAKE, 4, 512, 16, None, FAKE, FAKE, 3, None) == INVALID         # planes too short
+    assert f(FAKE, 4, 512, 16, None, FAKE, FAKE, -1, None) == INVALID
+    assert f(FAKE, 0, 512, 16, None, None, None, 0, None) == OK              # nothing to do
 
 
 def test_index_validation():
@@ -95,6 +97,18 @@ def test_index_validation():
     need = lib.csa2_workspace_size(1, 2, 100, 8, 16)
     assert call(wsb=need - 1) == WORKSPACE
     assert call(ws=FAKE + 8, wsb=need) == WORKSPACE       # workspace must be 256-B aligned
+    scan = lib.csa2_index_scan
+    assert scan(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, None, None) == INVALID
+    assert scan(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 101, FAKE, None) == INVALID
+    pool = lib.csa2_index_pool
+    assert pool(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, FAKE, 0, 16, FAKE, FAKE, FAKE,
+                FAKE, FAKE, 1 << 30, None) == INVALID     # pool stage needs k_blocks >= 1
+    assert pool(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, None, 8, 16, FAKE, FAKE, FAKE,
+                FAKE, FAKE, 1 << 30, None) == INVALID     # no block keys
+    assert pool(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, FAKE, 8, 16, FAKE, FAKE, FAKE,
+                FAKE, FAKE, 0, None) == WORKSPACE
+    assert lib.csa2_workspace_size(3, 2, 100, 0, 16) == 0
+    assert 0 < lib.csa2_workspace_size(3, 2, 100, 8, 16) < lib.csa2_workspace_size(1, 2, 100, 8, 16)
     re_ = lib.csa2_index_reindex
     assert re_(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, FAKE, None, 8, 16, FAKE, FAKE,
                FAKE, 1 << 30, None) == INVALID            # pool without counts

@@ -231,7 +231,7 @@ def attn_case(csa2, H, n_vis_list, topk_rows, swa_ends, seed=0, swa_len=200, win
     swa = W.swa_rows_e4m3(S * swa_len, 512, seed=seed + 99).reshape(S, swa_len, 512)
     R = len(topk_rows)
     q = W.bf16_normal((R, H, 512), seed=seed + 7)
-    k_pos = max(len(t) for t, _ in topk_rows)
+    k_pos = max(1, max(len(t) for t, _ in topk_rows))
     topk = np.full((R, k_pos), -1, np.int32)
     ntopk = np.zeros(R, np.int32)
     row_seq = np.zeros(R, np.int32)
