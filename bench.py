@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=4,
+    ap.add_argument("--cpu-rows", type=int, default=8,
                     help="query rows of the step the oracle runs for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ctx", type=int, default=None, help="override the context (testing only)")
@@ -88,6 +88,7 @@ def build(ctx_override=None):
         n_topk=[torch.empty(B, dtype=torch.int32, device=dev) for _ in range(L)],
         ws_pool=csa2.workspace(csa2.CSA2_OP_INDEX_POOL, B, T, wl.k_blk, wl.k_pos),
         ws_re=csa2.workspace(csa2.CSA2_OP_INDEX_REINDEX, B, T, wl.k_blk, wl.k_pos),
+        ws_attn=csa2.attn_workspace(B, H, wl.k_pos, wl.swa),
         o=torch.empty((B, H, 512), dtype=torch.float32, device=dev),
         lse=torch.empty((B, H), dtype=torch.float32, device=dev),
     )
@@ -120,7 +121,7 @@ def step(c, ev=None):
                                     c["ws_re"])
             src = l
         csa2.csa2_sparse_attn(cache, c["q"][l], seqs, c["topk"][src], c["n_topk"][src], SCALE,
-                              c["o"], c["lse"], swa=c["swa"][l])
+                              c["o"], c["lse"], swa=c["swa"][l], workspace=c["ws_attn"])
         if ev is not None:
             ev["layer"][l].record()
 
@@ -203,7 +204,7 @@ def cpu_baseline(c, rows):
 
     # the main latents of every entry the oracle will gather (from the same
     # generator), quantised by the oracle itself before timing
-    for s in range(rows):
+    def gathered_ids(s):
         ikc, iks = planes[s]
         ids = set()
         f = oracle.full_layer_select(qi[0][s], wv[0][s], ikc, iks, T, wl.k_blk, wl.k_pos)
@@ -212,7 +213,11 @@ def cpu_baseline(c, rows):
             if mode == "reindex":
                 r = oracle.reindex_select(qi[l][s], wv[l][s], ikc, iks, T, f["pool"], wl.k_pos)
                 ids.update(r["topk"][r["topk"] >= 0].tolist())
-        ids = np.array(sorted(ids), np.int64)
+        return np.array(sorted(ids), np.int64)
+
+    all_ids = oracle.parallel_map(gathered_ids, list(range(rows)), rows)
+    for s in range(rows):
+        ids = all_ids[s]
         lat = W.rms_rows(T - 1, 512, W.seed_for(seed, W.T_LATENT, 0, s), device="cuda")
         lat = torch.cat([lat, c["new_lat"][s:s + 1]])
         lat_rows[s] = oracle.quantize(lat[torch.from_numpy(ids).cuda()].cpu().numpy(), oracle.KV_GROUP)

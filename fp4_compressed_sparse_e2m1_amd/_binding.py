@@ -66,10 +66,13 @@ def load():
         lib.csa2_index_pool.restype = ctypes.c_int
         lib.csa2_index_reindex.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, P, P, P, sz, P]
         lib.csa2_index_reindex.restype = ctypes.c_int
-        lib.csa2_sparse_attn.argtypes = [P, P, i32, P, i32, P, P, i32, ctypes.c_float, P, P, P, P]
+        lib.csa2_sparse_attn.argtypes = [P, P, i32, P, i32, P, P, i32, ctypes.c_float, P, P, P, P,
+                                         sz, P]
         lib.csa2_sparse_attn.restype = ctypes.c_int
-        lib.csa2_swa_merge.argtypes = [P, i32, P, i32, P, i32, ctypes.c_float, P, P, P]
+        lib.csa2_swa_merge.argtypes = [P, i32, P, i32, P, i32, ctypes.c_float, P, P, P, sz, P]
         lib.csa2_swa_merge.restype = ctypes.c_int
+        lib.csa2_attn_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.csa2_attn_workspace_size.restype = sz
         lib.csa2_status_string.argtypes = [ctypes.c_int]
         lib.csa2_status_string.restype = ctypes.c_char_p
         lib.csa2_version.argtypes = []
@@ -244,29 +247,47 @@ def csa2_index_reindex(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, pool
     _check("csa2_index_reindex", st)
 
 
+def csa2_attn_workspace_size(n_rows: int, n_heads: int, k_pos: int, swa_window: int) -> int:
+    return int(load().csa2_attn_workspace_size(n_rows, n_heads, k_pos, swa_window))
+
+
+def attn_workspace(n_rows: int, n_heads: int, k_pos: int, swa_window: int, device="cuda"):
+    """Workspace for the split attention path, or None when no split is used."""
+    n = csa2_attn_workspace_size(n_rows, n_heads, k_pos, swa_window)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace, torch.uint8, "workspace"), workspace.numel()
+
+
 def csa2_sparse_attn(cache: Cache, q, row_seq, topk, n_topk, scale, o, lse, swa: Swa = None,
-                     stream=None):
+                     workspace=None, stream=None):
     R, H, D = q.shape
     if D != 512:
         raise ValueError("q must be [n_rows, n_heads, 512]")
     cs = cache.struct()
     ss = swa.struct() if swa is not None else None
+    wp, wb = _ws(workspace)
     st = load().csa2_sparse_attn(
         ctypes.byref(cs), _ptr(q, torch.bfloat16, "q"), H, _ptr(row_seq, torch.int32, "row_seq", (R,)),
         R, _ptr(topk, torch.int32, "topk"), _ptr(n_topk, torch.int32, "n_topk", (R,)),
         topk.shape[1], float(scale), ctypes.byref(ss) if ss is not None else None,
         _ptr(o, torch.float32, "o", (R, H, 512)), _ptr(lse, torch.float32, "lse", (R, H)),
-        _stream(stream))
+        wp, wb, _stream(stream))
     _check("csa2_sparse_attn", st)
 
 
-def csa2_swa_merge(q, row_seq, swa: Swa, scale, o, lse, stream=None):
+def csa2_swa_merge(q, row_seq, swa: Swa, scale, o, lse, workspace=None, stream=None):
     R, H, D = q.shape
     ss = swa.struct()
+    wp, wb = _ws(workspace)
     st = load().csa2_swa_merge(
         _ptr(q, torch.bfloat16, "q"), H, _ptr(row_seq, torch.int32, "row_seq", (R,)), R,
         ctypes.byref(ss), swa.kv.shape[0], float(scale), _ptr(o, torch.float32, "o", (R, H, 512)),
-        _ptr(lse, torch.float32, "lse", (R, H)), _stream(stream))
+        _ptr(lse, torch.float32, "lse", (R, H)), wp, wb, _stream(stream))
     _check("csa2_swa_merge", st)
 
 

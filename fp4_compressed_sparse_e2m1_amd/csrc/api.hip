@@ -269,6 +269,27 @@ bool swa_ok(const csa2_swa *s) {
          aligned(s->kv, 16);
 }
 
+int32_t attn_max_tiles(int32_t k_pos, int32_t window) {
+  return (k_pos + kAttnTileKeys - 1) / kAttnTileKeys + (window + kAttnTileKeys - 1) / kAttnTileKeys;
+}
+
+// Fills the split fields of `a`; CSA2_E_WORKSPACE if a workspace is given but
+// smaller than the plan needs.
+csa2_status attach_workspace(AttnArgs &a, int32_t n_rows, int32_t n_heads, int32_t max_tiles,
+                             void *workspace, size_t workspace_bytes) {
+  a.n_split = 1;
+  a.tiles_per_split = max_tiles;
+  if (!workspace) return CSA2_OK;
+  const AttnPlan p = plan_attention(n_rows, n_heads, max_tiles);
+  if (p.n_split <= 1) return CSA2_OK;
+  if (workspace_bytes < p.bytes || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
+  a.n_split = p.n_split;
+  a.tiles_per_split = p.tiles_per_split;
+  a.part_o = static_cast<float *>(workspace);
+  a.part_ml = a.part_o + (size_t)n_rows * p.n_split * n_heads * 512;
+  return CSA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -351,7 +372,8 @@ csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, c
 csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
                              const int32_t *row_seq, int32_t n_rows, const int32_t *topk,
                              const int32_t *n_topk, int32_t k_pos, float scale,
-                             const csa2_swa *swa, float *o, float *lse, void *stream) {
+                             const csa2_swa *swa, float *o, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream) {
   if (!cache_ok(cache, true, false)) return CSA2_E_INVALID_ARG;
   if (!q || !row_seq || !topk || !n_topk || !o || !lse) return CSA2_E_INVALID_ARG;
   if (n_rows < 0 || k_pos < 1 || !isfinite(scale)) return CSA2_E_INVALID_ARG;
@@ -360,7 +382,6 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   if (k_pos > kMaxAttnPos) return CSA2_E_UNSUPPORTED;
   if (swa && !swa_ok(swa)) return CSA2_E_INVALID_ARG;
   if (n_rows == 0) return CSA2_OK;
-  if (prepare() != hipSuccess) return CSA2_E_HIP;
   AttnArgs a = {};
   a.kv_codes = cache->kv_codes;
   a.kv_scales = cache->kv_scales;
@@ -381,19 +402,24 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   a.o = o;
   a.lse = lse;
   a.merge_in = 0;
+  const csa2_status ws = attach_workspace(a, n_rows, n_heads,
+                                          attn_max_tiles(k_pos, swa ? swa->window : 0), workspace,
+                                          workspace_bytes);
+  if (ws != CSA2_OK) return ws;
+  if (prepare() != hipSuccess) return CSA2_E_HIP;
   hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
 }
 
 csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *row_seq,
                            int32_t n_rows, const csa2_swa *swa, int32_t n_seq, float scale,
-                           float *o, float *lse, void *stream) {
+                           float *o, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream) {
   if (!q || !row_seq || !o || !lse || !swa_ok(swa)) return CSA2_E_INVALID_ARG;
   if (n_rows < 0 || n_seq < 1 || !isfinite(scale)) return CSA2_E_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(o, 4) || !aligned(lse, 4)) return CSA2_E_INVALID_ARG;
   if (n_heads != 16 && n_heads != 32 && n_heads != 64) return CSA2_E_UNSUPPORTED;
   if (n_rows == 0) return CSA2_OK;
-  if (prepare() != hipSuccess) return CSA2_E_HIP;
   AttnArgs a = {};
   a.cap = 1;
   a.n_seq = n_seq;
@@ -407,8 +433,20 @@ csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *ro
   a.o = o;
   a.lse = lse;
   a.merge_in = 1;
+  const csa2_status ws = attach_workspace(a, n_rows, n_heads, attn_max_tiles(0, swa->window),
+                                          workspace, workspace_bytes);
+  if (ws != CSA2_OK) return ws;
+  if (prepare() != hipSuccess) return CSA2_E_HIP;
   hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
+size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t k_pos,
+                                int32_t swa_window) {
+  if (n_rows < 0 || (n_heads != 16 && n_heads != 32 && n_heads != 64) || k_pos < 0 ||
+      k_pos > kMaxAttnPos || swa_window < 0 || swa_window > 1024)
+    return 0;
+  return plan_attention(n_rows, n_heads, attn_max_tiles(k_pos, swa_window)).bytes;
 }
 
 const char *csa2_status_string(csa2_status status) {

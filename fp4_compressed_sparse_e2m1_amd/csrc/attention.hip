@@ -31,7 +31,7 @@ namespace csa2 {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kTileKeys = 32;
+constexpr int kTileKeys = kAttnTileKeys;
 constexpr int kVtStride = 40;          // halves per Vt row (32 keys + pad)
 constexpr int kPStride = 40;           // halves per P row
 constexpr float kLazyRescale = 8.0f;   // log2 units
@@ -59,7 +59,10 @@ attn_kernel(AttnArgs a) {
   __shared__ int s_valid[kTileKeys];
   __shared__ int s_rescale;
 
-  const int r = blockIdx.x;
+  const int r = blockIdx.x / a.n_split;
+  const int sp = blockIdx.x - r * a.n_split;
+  const bool split = a.n_split > 1;
+  const bool merge_in = a.merge_in && !split;   // with a split the merge kernel folds (o, lse) in
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -84,7 +87,11 @@ attn_kernel(AttnArgs a) {
     n_s = (int)(end - s0);
   }
   const int n_gt = (n_g + kTileKeys - 1) / kTileKeys;
-  const int n_tiles = n_gt + (n_s + kTileKeys - 1) / kTileKeys;
+  const int n_all = n_gt + (n_s + kTileKeys - 1) / kTileKeys;
+  // this work-group's tiles: [t_begin, t_end)
+  const int t_begin = split ? sp * a.tiles_per_split : 0;
+  int t_end = split ? t_begin + a.tiles_per_split : n_all;
+  t_end = t_end < n_all ? t_end : n_all;
 
   // Q operand: qa[hb][t] = q[r][16hb + c][128w + 32G + 8t .. +7] in f16.
   f16x8 qa[HB][4];
@@ -103,7 +110,7 @@ attn_kernel(AttnArgs a) {
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc_o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (a.merge_in) {
+  if (merge_in) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -119,7 +126,7 @@ attn_kernel(AttnArgs a) {
   }
   if (tid < H) {
     float m0 = -INFINITY, l0 = 0.f;
-    if (a.merge_in) {
+    if (merge_in) {
       const float lin = a.lse[(int64_t)r * H + tid];
       if (lin != -INFINITY) {
         m0 = lin * 1.4426950408889634f;
@@ -167,11 +174,11 @@ attn_kernel(AttnArgs a) {
   };
 
   RawTile cur;
-  if (n_tiles > 0) cur = load_tile(0);
+  if (t_begin < t_end) cur = load_tile(t_begin);
 
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  for (int tile = t_begin; tile < t_end; ++tile) {
     RawTile nxt;
-    if (tile + 1 < n_tiles) nxt = load_tile(tile + 1);
+    if (tile + 1 < t_end) nxt = load_tile(tile + 1);
     const bool is_swa = tile >= n_gt;
 
     // dequantise this wave's quarter of the 32 keys
@@ -296,6 +303,24 @@ attn_kernel(AttnArgs a) {
   }
 
   __syncthreads();
+  if (split) {
+    // unnormalised partial: O, running max (log2 units) and sum per head
+    const int64_t part = (int64_t)r * a.n_split + sp;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * hb + 4 * G + i;
+        float *prow = a.part_o + (part * H + h) * 512 + 128 * w + c;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) prow[16 * db] = acc_o[hb][db][i];
+      }
+    if (tid < H) {
+      a.part_ml[(part * H + tid) * 2] = s_m[tid];
+      a.part_ml[(part * H + tid) * 2 + 1] = s_l[tid];
+    }
+    return;
+  }
   // normalise and store
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
@@ -316,18 +341,87 @@ attn_kernel(AttnArgs a) {
   }
 }
 
+// Merge of the split partials of one (row, head): the softmax over the union
+// of the splits' key sets (and of the earlier result in (o, lse) when
+// merge_in is set), by their log-sum-exp.
+__global__ void __launch_bounds__(256)
+attn_merge_kernel(AttnArgs a, int H) {
+  const int r = blockIdx.x / H;
+  const int h = blockIdx.x - r * H;
+  const int tid = threadIdx.x;
+  const float *ml = a.part_ml + ((int64_t)r * a.n_split * H + h) * 2;
+  float M = -INFINITY;
+  float m_in = -INFINITY;
+  if (a.merge_in) {
+    const float lin = a.lse[(int64_t)r * H + h];
+    if (lin != -INFINITY) m_in = lin * 1.4426950408889634f;
+    M = m_in;
+  }
+  for (int s = 0; s < a.n_split; ++s) {
+    const float l = ml[(int64_t)s * H * 2 + 1];
+    if (l > 0.f) M = fmaxf(M, ml[(int64_t)s * H * 2]);
+  }
+  float L = 0.f;
+  float acc0 = 0.f, acc1 = 0.f;
+  const int d0 = tid, d1 = tid + 256;
+  if (M != -INFINITY) {
+    if (m_in != -INFINITY) {
+      const float wgt = exp2f(m_in - M);
+      L += wgt;
+      const float *oin = a.o + ((int64_t)r * H + h) * 512;
+      acc0 += wgt * oin[d0];
+      acc1 += wgt * oin[d1];
+    }
+    for (int s = 0; s < a.n_split; ++s) {
+      const float l = ml[(int64_t)s * H * 2 + 1];
+      if (!(l > 0.f)) continue;
+      const float wgt = exp2f(ml[(int64_t)s * H * 2] - M);
+      L += wgt * l;
+      const float *po = a.part_o + (((int64_t)r * a.n_split + s) * H + h) * 512;
+      acc0 += wgt * po[d0];
+      acc1 += wgt * po[d1];
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float *orow = a.o + ((int64_t)r * H + h) * 512;
+  orow[d0] = acc0 * inv;
+  orow[d1] = acc1 * inv;
+  if (tid == 0)
+    a.lse[(int64_t)r * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+}
+
 }  // namespace
 
 hipError_t prepare_attention() { return hipSuccess; }
 
+AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t max_tiles) {
+  AttnPlan p = {1, max_tiles > 0 ? max_tiles : 1, 0};
+  // Few rows leave most of the 256 CUs idle: spread each row's key tiles over
+  // several work-groups (about 384 in all).  Many rows fill the GPU already,
+  // and splitting them would only add partial-result traffic.
+  if (n_rows >= 192 || max_tiles <= 1) return p;
+  int split = (384 + n_rows - 1) / n_rows;
+  split = split < max_tiles ? split : max_tiles;
+  const int tps = (max_tiles + split - 1) / split;
+  split = (max_tiles + tps - 1) / tps;
+  if (split <= 1) return p;
+  p.n_split = split;
+  p.tiles_per_split = tps;
+  p.bytes = (size_t)n_rows * split * n_heads * (512 + 2) * sizeof(float);
+  return p;
+}
+
 hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  dim3 grid((unsigned)n_rows);
+  dim3 grid((unsigned)(n_rows * a.n_split));
   switch (n_heads) {
     case 16: attn_kernel<1><<<grid, kAttnThreads, 0, stream>>>(a); break;
     case 32: attn_kernel<2><<<grid, kAttnThreads, 0, stream>>>(a); break;
     default: attn_kernel<4><<<grid, kAttnThreads, 0, stream>>>(a); break;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split <= 1) return e;
+  attn_merge_kernel<<<dim3((unsigned)(n_rows * n_heads)), 256, 0, stream>>>(a, n_heads);
   return hipGetLastError();
 }
 

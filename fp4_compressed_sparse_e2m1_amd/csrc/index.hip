@@ -35,11 +35,17 @@ namespace csa2 {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kTilesPerWave = kScoreChunk / (4 * 16);   // 16 tiles of 16 entries
+
+// Entries per work-group: long contiguous runs for the scan, short ones for the
+// pool gather (its pool-id -> key loads form a dependent chain).
+template <int MODE>
+constexpr int score_chunk() { return MODE == kScorePool ? kScorePoolChunk : kScoreChunk; }
 
 template <int MODE>
 __global__ void __launch_bounds__(kScoreThreads)
 score_kernel(ScoreArgs a) {
+  constexpr int kChunk = score_chunk<MODE>();
+  constexpr int kTilesPerWave = kChunk / (4 * 16);
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -60,7 +66,7 @@ score_kernel(ScoreArgs a) {
   }
   // slots of this row: entries (scan / flat) or candidate slots (pool)
   const int64_t n_slots = (MODE == kScorePool) ? (int64_t)8 * a.k_blocks : (int64_t)n_vis;
-  const int64_t chunk0 = (int64_t)blockIdx.x * kScoreChunk;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kChunk;
   if (chunk0 >= n_slots) return;
 
   // Query operand: lane (G, c) holds head c's channels 32G + 8t .. +7, t = 0..3.
@@ -208,9 +214,22 @@ select_kernel(SelectArgs a) {
     uint32_t prefix = 0u, mask = 0u;
     int k_rem = k_eff;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < n; i += kSelThreads) {
-        const uint32_t k = skeys[i];
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      // Histogram of the current digit over keys that match the prefix.  Most
+      // keys share a few leading digits, so lanes holding the same bin as the
+      // wave's first active lane add their count with one atomic.
+      for (int base = wave * 64; base < n; base += kSelThreads) {
+        const int i = base + lane;
+        const uint32_t k = i < n ? skeys[i] : 0u;
+        const bool m = i < n && (k & mask) == prefix;
+        const uint32_t bin = (k >> shift) & 255u;
+        const unsigned long long act = __ballot(m);
+        if (act) {
+          const int leader = __ffsll((long long)act) - 1;
+          const uint32_t lb = __shfl(bin, leader);
+          const unsigned long long same = __ballot(m && bin == lb);
+          if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+          if (m && bin != lb) atomicAdd(&hist[bin], 1u);
+        }
       }
       __syncthreads();
       if (wave == 0) {
@@ -327,7 +346,8 @@ select_kernel(SelectArgs a) {
 
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int64_t slots,
                         hipStream_t stream) {
-  const int64_t chunks = (slots + kScoreChunk - 1) / kScoreChunk;
+  const int chunk = mode == kScorePool ? kScorePoolChunk : kScoreChunk;
+  const int64_t chunks = (slots + chunk - 1) / chunk;
   if (chunks == 0 || n_rows == 0) return hipSuccess;
   dim3 grid((unsigned)chunks, (unsigned)n_rows);
   switch (mode) {

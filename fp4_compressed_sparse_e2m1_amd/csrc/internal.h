@@ -27,8 +27,9 @@ struct ScoreArgs {
   int64_t out_stride;
 };
 
-// Entries per work-group of the scoring kernel.
+// Entries per work-group of the scoring kernel (scan / flat, and pool mode).
 constexpr int kScoreChunk = 1024;
+constexpr int kScorePoolChunk = 256;
 
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int64_t slots,
                         hipStream_t stream);
@@ -86,7 +87,25 @@ struct AttnArgs {
   float *o;                   // [R][H][512]
   float *lse;                 // [R][H]
   int32_t merge_in;           // 1: start from (o, lse) as an earlier result
+  // split of a row's key tiles over several work-groups (n_split > 1):
+  // unnormalised partial results, merged by a second kernel
+  int32_t n_split;
+  int32_t tiles_per_split;
+  float *part_o;              // [R][n_split][H][512]
+  float *part_ml;             // [R][n_split][H][2]  (running max in log2 units, sum)
 };
+
+// Key tiles per attention work-group step.
+constexpr int kAttnTileKeys = 32;
+
+// Work-group split of the attention rows: n_split partial results per row
+// (1 = no split, no workspace).
+struct AttnPlan {
+  int32_t n_split;
+  int32_t tiles_per_split;
+  size_t bytes;
+};
+AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t max_tiles);
 
 hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, hipStream_t stream);
 hipError_t prepare_attention();

@@ -222,11 +222,16 @@ csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, c
  * Types: q bf16 bits [n_rows][n_heads][512]; topk int32 [n_rows][k_pos];
  * n_topk int32 [n_rows]; o fp32 [n_rows][n_heads][512]; lse fp32
  * [n_rows][n_heads].  Requires n_heads in {16, 32, 64}, n_rows >= 0,
- * 1 <= k_pos <= 65536, scale finite. */
+ * 1 <= k_pos <= 65536, scale finite.
+ * workspace (optional, 256-B aligned, csa2_attn_workspace_size bytes): with
+ * it, a small batch spreads each row's keys over several work-groups and
+ * merges their partial results; with workspace == NULL every row runs in one
+ * work-group (same results up to fp32 rounding order, slower for few rows). */
 csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
                              const int32_t *row_seq, int32_t n_rows, const int32_t *topk,
                              const int32_t *n_topk, int32_t k_pos, float scale,
-                             const csa2_swa *swa, float *o, float *lse, void *stream);
+                             const csa2_swa *swa, float *o, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* S6 -- SWA branch and log-sum-exp merge [P3 "전역 어텐션과 지역 어텐션";
  * the merge is the softmax over the union of the two key sets].
@@ -236,10 +241,19 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
  * the result over G ∪ S:
  *   m = max(lse_G, lse_S); o = (e^(lse_G-m) o_G + e^(lse_S-m) o_S) /
  *   (e^(lse_G-m) + e^(lse_S-m)); lse = m + log(e^(lse_G-m) + e^(lse_S-m)).
- * Same types and limits as csa2_sparse_attn; swa must not be NULL. */
+ * Same types, limits and workspace rule as csa2_sparse_attn; swa must not be
+ * NULL. */
 csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *row_seq,
                            int32_t n_rows, const csa2_swa *swa, int32_t n_seq, float scale,
-                           float *o, float *lse, void *stream);
+                           float *o, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Scratch bytes that lets csa2_sparse_attn (k_pos, swa_window = the SWA
+ * window or 0 without SWA) or csa2_swa_merge (k_pos = 0) split its rows over
+ * several work-groups; 0 when no split is used for these sizes (a NULL
+ * workspace is then fine).  Returns 0 for invalid arguments. */
+size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t k_pos,
+                                int32_t swa_window);
 
 /* Human-readable name of a status code (static string). */
 const char *csa2_status_string(csa2_status status);

@@ -120,7 +120,7 @@ def test_attention_validation():
     lib = csa2.load()
     c = cache_struct()
     f = lib.csa2_sparse_attn
-    base = [ctypes.byref(c), FAKE, 16, FAKE, 4, FAKE, FAKE, 512, 0.04, None, FAKE, FAKE, None]
+    base = [ctypes.byref(c), FAKE, 16, FAKE, 4, FAKE, FAKE, 512, 0.04, None, FAKE, FAKE, None, 0, None]
 
     def call(i, v):
         a = list(base)
@@ -139,10 +139,21 @@ def test_attention_validation():
     assert call(9, ctypes.byref(bad_swa)) == INVALID
     m = lib.csa2_swa_merge
     good_swa = B._SwaStruct(FAKE, 128, FAKE, 128)
-    assert m(FAKE, 16, FAKE, 4, None, 1, 0.04, FAKE, FAKE, None) == INVALID
-    assert m(FAKE, 16, FAKE, 4, ctypes.byref(good_swa), 0, 0.04, FAKE, FAKE, None) == INVALID
-    assert m(FAKE, 20, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None) == UNSUPPORTED
-    assert m(FAKE, 16, FAKE, 0, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None) == OK
+    assert m(FAKE, 16, FAKE, 4, None, 1, 0.04, FAKE, FAKE, None, 0, None) == INVALID
+    assert m(FAKE, 16, FAKE, 4, ctypes.byref(good_swa), 0, 0.04, FAKE, FAKE, None, 0, None) == INVALID
+    assert m(FAKE, 20, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == UNSUPPORTED
+    assert m(FAKE, 16, FAKE, 0, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == OK
+    # a split needs its workspace: given but too small is an error, NULL is not
+    ws = lib.csa2_attn_workspace_size(8, 16, 512, 128)
+    assert ws >= 8 * 2 * 16 * 514 * 4
+    assert lib.csa2_attn_workspace_size(256, 64, 512, 128) == 0      # many rows: no split
+    assert lib.csa2_attn_workspace_size(8, 24, 512, 128) == 0        # invalid heads
+    a = list(base)
+    a[12], a[13] = FAKE, 64                                           # split planned, 64 B given
+    assert f(*a) == WORKSPACE
+    a[12] = FAKE + 8
+    a[13] = 1 << 30
+    assert f(*a) == WORKSPACE                                         # misaligned workspace
 
 
 def test_binding_rejects_host_tensors():

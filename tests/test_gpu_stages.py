@@ -251,8 +251,9 @@ def oracle_attn(c, r):
     return oracle.attend_row(W.bf16_bits(c["q"][r]), kvc, kvs, c["topk"][r][:c["ntopk"][r]], rows, SCALE)
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["one_wg_per_row", "split_rows"])
 @pytest.mark.parametrize("H", [16, 64])
-def test_sparse_attn_global_fused_and_merge(csa2, H):
+def test_sparse_attn_global_fused_and_merge(csa2, H, split):
     rng = np.random.default_rng(H)
     nv = [3000, 700]
     rows = [(np.sort(rng.choice(3000, 512, replace=False)), 0),      # full Top-512
@@ -269,34 +270,43 @@ def test_sparse_attn_global_fused_and_merge(csa2, H):
     ntopk = dev(c["ntopk"])
     swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), c["window"])
     refs = [oracle_attn(c, r) for r in range(R)]      # the oracle skips -1 ids as well
+    k_pos = c["topk"].shape[1]
+    ws_g = csa2.attn_workspace(R, H, k_pos, 0) if split else None
+    ws_m = csa2.attn_workspace(R, H, 0, 128) if split else None
+    ws_f = csa2.attn_workspace(R, H, k_pos, 128) if split else None
+    if split:
+        assert ws_g is not None and ws_m is not None and ws_f is not None
     # global branch only
     o = torch.empty((R, H, 512), device="cuda")
     lse = torch.empty((R, H), device="cuda")
-    csa2.csa2_sparse_attn(cache, q, row_seq, topk, ntopk, SCALE, o, lse)
+    csa2.csa2_sparse_attn(cache, q, row_seq, topk, ntopk, SCALE, o, lse, workspace=ws_g)
     torch.cuda.synchronize()
     check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o_g"] for x in refs]),
                     np.stack([x["lse_g"] for x in refs]), "global")
     # then the SWA branch merged onto it
-    csa2.csa2_swa_merge(q, row_seq, swa, SCALE, o, lse)
+    csa2.csa2_swa_merge(q, row_seq, swa, SCALE, o, lse, workspace=ws_m)
     torch.cuda.synchronize()
     check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o"] for x in refs]),
                     np.stack([x["lse"] for x in refs]), "merged")
     # fused: both branches in one softmax
     o2 = torch.empty_like(o)
     lse2 = torch.empty_like(lse)
-    csa2.csa2_sparse_attn(cache, q, row_seq, topk, ntopk, SCALE, o2, lse2, swa=swa)
+    csa2.csa2_sparse_attn(cache, q, row_seq, topk, ntopk, SCALE, o2, lse2, swa=swa, workspace=ws_f)
     torch.cuda.synchronize()
     check_attention(o2.cpu().numpy(), lse2.cpu().numpy(), np.stack([x["o"] for x in refs]),
                     np.stack([x["lse"] for x in refs]), "fused")
 
 
-def test_attention_empty_everything(csa2):
-    c = attn_case(csa2, 16, [100], [(np.array([], np.int64), 0)], swa_ends=[0], seed=3)
-    o = torch.full((1, 16, 512), 5.0, device="cuda")
-    lse = torch.zeros((1, 16), device="cuda")
+@pytest.mark.parametrize("split", [False, True])
+def test_attention_empty_everything(csa2, split):
+    rows = [(np.array([], np.int64), 0), (np.array([-1, -1], np.int64), 0)]
+    c = attn_case(csa2, 16, [100], rows, swa_ends=[0, -5], seed=3)
+    o = torch.full((2, 16, 512), 5.0, device="cuda")
+    lse = torch.zeros((2, 16), device="cuda")
     swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), 128)
+    ws = csa2.attn_workspace(2, 16, c["topk"].shape[1], 128) if split else None
     csa2.csa2_sparse_attn(c["cache"], dev(c["q"]), dev(c["row_seq"]), dev(c["topk"]),
-                          dev(c["ntopk"]), SCALE, o, lse, swa=swa)
+                          dev(c["ntopk"]), SCALE, o, lse, swa=swa, workspace=ws)
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
 
