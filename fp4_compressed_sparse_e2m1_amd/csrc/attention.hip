@@ -32,6 +32,7 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kTileKeys = kAttnTileKeys;
+constexpr int kMergeSplitLimit = 64;     // splits the merge kernel accepts
 constexpr int kVtStride = 40;          // halves per Vt row (32 keys + pad)
 constexpr int kPStride = 40;           // halves per P row
 constexpr float kLazyRescale = 8.0f;   // log2 units
@@ -341,53 +342,97 @@ attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the split partials of one (row, head): the softmax over the union
-// of the splits' key sets (and of the earlier result in (o, lse) when
-// merge_in is set), by their log-sum-exp.
+// Merge of the split partials of a row: the softmax over the union of the
+// splits' key sets (and of the earlier result in (o, lse) when merge_in is
+// set), by their log-sum-exp.  A block handles 2 heads x 512 channels of one
+// row (4 outputs per thread); the per-split maxima and sums are staged in LDS.
+constexpr int kMergeMaxSplit = kMergeSplitLimit;
+
 __global__ void __launch_bounds__(256)
 attn_merge_kernel(AttnArgs a, int H) {
-  const int r = blockIdx.x / H;
-  const int h = blockIdx.x - r * H;
+  __shared__ float s_w[2][kMergeMaxSplit + 1];   // weight of each split (+ the earlier result)
+  __shared__ float s_L[2], s_M[2];
+  const int per_row = H / 2;
+  const int r = blockIdx.x / per_row;
+  const int h0 = 2 * (blockIdx.x - r * per_row);
   const int tid = threadIdx.x;
-  const float *ml = a.part_ml + ((int64_t)r * a.n_split * H + h) * 2;
-  float M = -INFINITY;
-  float m_in = -INFINITY;
-  if (a.merge_in) {
-    const float lin = a.lse[(int64_t)r * H + h];
-    if (lin != -INFINITY) m_in = lin * 1.4426950408889634f;
-    M = m_in;
-  }
-  for (int s = 0; s < a.n_split; ++s) {
-    const float l = ml[(int64_t)s * H * 2 + 1];
-    if (l > 0.f) M = fmaxf(M, ml[(int64_t)s * H * 2]);
-  }
-  float L = 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
-  const int d0 = tid, d1 = tid + 256;
-  if (M != -INFINITY) {
-    if (m_in != -INFINITY) {
-      const float wgt = exp2f(m_in - M);
-      L += wgt;
-      const float *oin = a.o + ((int64_t)r * H + h) * 512;
-      acc0 += wgt * oin[d0];
-      acc1 += wgt * oin[d1];
+  const int ns = a.n_split;
+  // wave 0 weighs the splits of head h0, wave 1 those of head h0 + 1; lane s
+  // holds split s
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  if (wv < 2) {
+    const int h = h0 + wv;
+    float m_in = -INFINITY;
+    if (a.merge_in) {
+      const float lin = a.lse[(int64_t)r * H + h];
+      if (lin != -INFINITY) m_in = lin * 1.4426950408889634f;
     }
-    for (int s = 0; s < a.n_split; ++s) {
-      const float l = ml[(int64_t)s * H * 2 + 1];
-      if (!(l > 0.f)) continue;
-      const float wgt = exp2f(ml[(int64_t)s * H * 2] - M);
-      L += wgt * l;
-      const float *po = a.part_o + (((int64_t)r * a.n_split + s) * H + h) * 512;
-      acc0 += wgt * po[d0];
-      acc1 += wgt * po[d1];
+    float m = -INFINITY, l = 0.f;
+    if (lane < ns) {
+      const float *ml = a.part_ml + (((int64_t)r * ns + lane) * H + h) * 2;
+      m = ml[0];
+      l = ml[1];
     }
+    float M = (l > 0.f) ? m : -INFINITY;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    M = fmaxf(M, m_in);
+    const float wgt = (l > 0.f && M != -INFINITY) ? exp2f(m - M) : 0.f;
+    float L = wgt * l;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    const float win = (m_in != -INFINITY) ? exp2f(m_in - M) : 0.f;
+    L += win;
+    if (lane < ns) s_w[wv][lane] = wgt;
+    if (lane == 0) {
+      s_w[wv][ns] = win;
+      s_L[wv] = L;
+      s_M[wv] = M;
+    }
+  }
+  __syncthreads();
+  const int hh = tid >> 7;                 // which of the two heads
+  const int d = (tid & 127) * 4;           // four channels
+  const int h = h0 + hh;
+  const float L = s_L[hh];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float *po = a.part_o + (((int64_t)r * ns) * H + h) * 512 + d;
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4 *>(po + (int64_t)(s + u) * H * 512);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wgt = s_w[hh][s + u];
+      acc.x += wgt * v[u].x;
+      acc.y += wgt * v[u].y;
+      acc.z += wgt * v[u].z;
+      acc.w += wgt * v[u].w;
+    }
+  }
+  for (; s < ns; ++s) {
+    const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)s * H * 512);
+    const float wgt = s_w[hh][s];
+    acc.x += wgt * v.x;
+    acc.y += wgt * v.y;
+    acc.z += wgt * v.z;
+    acc.w += wgt * v.w;
+  }
+  float4 *orow = reinterpret_cast<float4 *>(a.o + ((int64_t)r * H + h) * 512 + d);
+  const float win = s_w[hh][ns];
+  if (win > 0.f) {
+    const float4 oi = *orow;
+    acc.x += win * oi.x;
+    acc.y += win * oi.y;
+    acc.z += win * oi.z;
+    acc.w += win * oi.w;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float *orow = a.o + ((int64_t)r * H + h) * 512;
-  orow[d0] = acc0 * inv;
-  orow[d1] = acc1 * inv;
-  if (tid == 0)
-    a.lse[(int64_t)r * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  *orow = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if ((tid & 127) == 0)
+    a.lse[(int64_t)r * H + h] = L > 0.f ? (s_M[hh] + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
 }  // namespace
@@ -399,11 +444,14 @@ AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t max_tiles) {
   // Few rows leave most of the 256 CUs idle: spread each row's key tiles over
   // several work-groups (about 384 in all).  Many rows fill the GPU already,
   // and splitting them would only add partial-result traffic.
-  if (n_rows >= 192 || max_tiles <= 1) return p;
-  int split = (384 + n_rows - 1) / n_rows;
+  if (n_rows >= 192 || max_tiles <= 2) return p;
+  int split = (256 + n_rows - 1) / n_rows;
   split = split < max_tiles ? split : max_tiles;
-  const int tps = (max_tiles + split - 1) / split;
+  int tps = (max_tiles + split - 1) / split;
+  tps = tps < 2 ? 2 : tps;                 // at least two tiles, so loads overlap compute
   split = (max_tiles + tps - 1) / tps;
+  split = split < kMergeSplitLimit ? split : kMergeSplitLimit;
+  tps = (max_tiles + split - 1) / split;
   if (split <= 1) return p;
   p.n_split = split;
   p.tiles_per_split = tps;
@@ -421,7 +469,7 @@ hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split <= 1) return e;
-  attn_merge_kernel<<<dim3((unsigned)(n_rows * n_heads)), 256, 0, stream>>>(a, n_heads);
+  attn_merge_kernel<<<dim3((unsigned)(n_rows * n_heads / 2)), 256, 0, stream>>>(a, n_heads);
   return hipGetLastError();
 }
 

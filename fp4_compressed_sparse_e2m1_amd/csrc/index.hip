@@ -185,13 +185,24 @@ select_kernel(SelectArgs a) {
   int n = (int)((int64_t)n_row - start);
   n = n < 0 ? 0 : (n > kSelectChunk ? kSelectChunk : n);
 
-  // load keys, count the valid (non-zero) ones
+  // load keys (all loads of a thread in flight at once), count the valid
+  // (non-zero) ones
   const uint32_t *kin = a.keys_in + (int64_t)r * a.in_stride + start;
   int nvalid = 0;
-  for (int i = tid; i < n; i += kSelThreads) {
-    const uint32_t k = kin[i];
-    skeys[i] = k;
-    nvalid += (k != 0u);
+  {
+    constexpr int PER = kSelectChunk / kSelThreads;
+    uint32_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = j * kSelThreads + tid;
+      v[j] = i < n ? kin[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = j * kSelThreads + tid;
+      if (i < n) skeys[i] = v[j];
+      nvalid += (v[j] != 0u);
+    }
   }
   if (tid < 256) hist[tid] = 0;
 #pragma unroll
@@ -292,7 +303,18 @@ select_kernel(SelectArgs a) {
   int eq_rank = eq_base + eq_in - eq;
   int pos = gt_base + gt_in - gt + (eq_rank < k_eq ? eq_rank : k_eq);
 
-  const int32_t *idin = a.ids_in ? a.ids_in + (int64_t)r * a.in_stride + start : nullptr;
+  // ids of this thread's range, fetched together (a later level carries the
+  // ids of the survivors; the first level uses positions)
+  constexpr int kMaxPer = kSelectChunk / kSelThreads;
+  int32_t ids[kMaxPer];
+  {
+    const int32_t *idin = a.ids_in ? a.ids_in + (int64_t)r * a.in_stride + start : nullptr;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int i = b0 + j;
+      ids[j] = (idin && i < b1) ? idin[i] : (int)(start + i);
+    }
+  }
   if (FINAL) {
     int32_t *out = a.out + (int64_t)r * a.k;
     int np = 0;
@@ -300,7 +322,10 @@ select_kernel(SelectArgs a) {
       np = a.n_pool[r];
       np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
     }
-    for (int i = b0; i < b1; ++i) {
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int i = b0 + j;
+      if (i >= b1) break;
       const uint32_t k = skeys[i];
       bool take = k > thr;
       if (k == thr) {
@@ -308,7 +333,7 @@ select_kernel(SelectArgs a) {
         ++eq_rank;
       }
       if (take) {
-        int id = idin ? idin[i] : (int)(start + i);
+        int id = ids[j];
         if (a.map_kind == kMapPool) {
           const int p = id >> 3;
           const int b = (p < np) ? a.pool_blocks[(int64_t)r * a.k_blocks + p] : -1;
@@ -322,7 +347,10 @@ select_kernel(SelectArgs a) {
   } else {
     uint32_t *kout = a.keys_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
     int32_t *iout = a.ids_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
-    for (int i = b0; i < b1; ++i) {
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int i = b0 + j;
+      if (i >= b1) break;
       const uint32_t k = skeys[i];
       bool take = k > thr;
       if (k == thr) {
@@ -331,7 +359,7 @@ select_kernel(SelectArgs a) {
       }
       if (take) {
         kout[pos] = k;
-        iout[pos] = idin ? idin[i] : (int)(start + i);
+        iout[pos] = ids[j];
         ++pos;
       }
     }
