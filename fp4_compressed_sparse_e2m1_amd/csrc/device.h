@@ -69,6 +69,39 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(uint4 v) {
                bf16_to_f16(v.w & 0xFFFF), bf16_to_f16(v.w >> 16)};
 }
 
+// max(x, 0) in one instruction: median of x, 0 and the largest float (+inf
+// inputs, outside the contract, would clamp to that value).
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
+
+// max(a, b) in one instruction: median of a, b and the largest float.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.402823466e38f); }
+
+// Lane permutations inside a row of 16 lanes (DPP): XOR 1 and XOR 2 within a
+// quad, mirror within each half row of 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within each 8 lanes
+constexpr int kDppRowRor8 = 0x128;     // lane i <- lane (i + 8) mod 16 within each 16 lanes
+
+// Maximum over each aligned group of 8 lanes, in every lane of the group.
+__device__ __forceinline__ float max8(float m) {
+  m = fmax2(m, dpp<kDppXor1>(m));
+  m = fmax2(m, dpp<kDppXor2>(m));
+  return fmax2(m, dpp<kDppHalfMirror>(m));
+}
+
+// Value of lane l + 16 for lanes 0..15 (and 32..47): the odd 16-lane rows are
+// swapped into the even ones.
+__device__ __forceinline__ float from_next_row(float x) {
+  const int xi = __float_as_int(x);
+  const auto sw = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  return __int_as_float(sw[1]);
+}
+
 // D = A(16x32) * B(32x16) + C on the matrix cores.  Lane l holds
 // A[l % 16][8*(l/16) .. +7], B[8*(l/16) .. +7][l % 16] and
 // C[4*(l/16) .. +3][l % 16].

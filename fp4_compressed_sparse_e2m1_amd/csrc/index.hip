@@ -41,12 +41,14 @@ constexpr int kScoreThreads = 256;
 template <int MODE>
 constexpr int score_chunk() { return MODE == kScorePool ? kScorePoolChunk : kScoreChunk; }
 
-template <int MODE>
+template <int MODE, int U = (MODE == kScorePool ? 4 : 2), int CHUNK = score_chunk<MODE>(),
+          bool ILV = false, bool ROWFAST = false>
 __global__ void __launch_bounds__(kScoreThreads)
 score_kernel(ScoreArgs a) {
-  constexpr int kChunk = score_chunk<MODE>();
+  constexpr int kChunk = CHUNK;
   constexpr int kTilesPerWave = kChunk / (4 * 16);
-  const int r = blockIdx.y;
+  const int r = ROWFAST ? blockIdx.x : blockIdx.y;
+  const int chunk_id = ROWFAST ? blockIdx.y : blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int G = lane >> 4;
@@ -66,7 +68,7 @@ score_kernel(ScoreArgs a) {
   }
   // slots of this row: entries (scan / flat) or candidate slots (pool)
   const int64_t n_slots = (MODE == kScorePool) ? (int64_t)8 * a.k_blocks : (int64_t)n_vis;
-  const int64_t chunk0 = (int64_t)blockIdx.x * kChunk;
+  const int64_t chunk0 = (int64_t)chunk_id * kChunk;
   if (chunk0 >= n_slots) return;
 
   // Query operand: lane (G, c) holds head c's channels 32G + 8t .. +7, t = 0..3.
@@ -89,17 +91,19 @@ score_kernel(ScoreArgs a) {
   const uint8_t *scales_base = a.ik_scales + (int64_t)seq * a.cap * 4;
   uint32_t *out_row = a.keys_out + (int64_t)r * a.out_stride;
 
-  const int64_t wave0 = chunk0 + (int64_t)wave * kTilesPerWave * 16;
-  constexpr int U = 4;
+  // tile t of this wave: contiguous per wave, or interleaved across the 4 waves
+  auto tile_slot0 = [&](int t) -> int64_t {
+    return ILV ? chunk0 + ((int64_t)t * 4 + wave) * 16 : chunk0 + ((int64_t)wave * kTilesPerWave + t) * 16;
+  };
   for (int tb = 0; tb < kTilesPerWave; tb += U) {
-    if (wave0 + (int64_t)tb * 16 >= n_slots) break;
+    if (tile_slot0(tb) >= n_slots) break;
     uint4 craw[U];
     uint32_t sraw[U];
     int64_t slot[U];
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      slot[u] = wave0 + (int64_t)(tb + u) * 16 + c;
+      slot[u] = tile_slot0(tb + u) + c;
       int64_t entry;
       if (MODE == kScorePool) {
         const int64_t p = slot[u] >> 3;
@@ -125,14 +129,11 @@ score_kernel(ScoreArgs a) {
       acc = mfma16x16x32(qa[2], e2m1x8_to_f16(craw[u].z) * sv, acc);
       acc = mfma16x16x32(qa[3], e2m1x8_to_f16(craw[u].w) * sv, acc);
       // lane (G, c): d[head 4G + i][entry c]; heads 8..15 are zero padding
-      float part = wh[0] * fmaxf(acc[0], 0.f) + wh[1] * fmaxf(acc[1], 0.f);
-      part += wh[2] * fmaxf(acc[2], 0.f) + wh[3] * fmaxf(acc[3], 0.f);
-      const float score = part + __shfl_down(part, 16);   // heads 0..3 + heads 4..7
+      float part = wh[0] * relu(acc[0]) + wh[1] * relu(acc[1]);
+      part += wh[2] * relu(acc[2]) + wh[3] * relu(acc[3]);
+      const float score = part + from_next_row(part);     // heads 0..3 + heads 4..7
       if (MODE == kScoreBlockMax) {
-        float m = valid[u] ? score : -INFINITY;
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
+        const float m = max8(valid[u] ? score : -INFINITY);
         const int64_t blk = slot[u] >> 3;
         if (lane < 16 && (c & 7) == 0 && blk * 8 < n_slots) out_row[blk] = score_key(m);
       } else if (MODE == kScoreFlat) {

@@ -28,7 +28,7 @@ struct ScoreArgs {
 };
 
 // Entries per work-group of the scoring kernel (scan / flat, and pool mode).
-constexpr int kScoreChunk = 1024;
+constexpr int kScoreChunk = 512;
 constexpr int kScorePoolChunk = 256;
 
 hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int64_t slots,
