@@ -279,91 +279,71 @@ select_kernel(SelectArgs a) {
     k_eq = k_rem;
   }
 
-  // ordered compaction: thread tid owns positions [tid*per, (tid+1)*per)
-  const int per = (n + kSelThreads - 1) / kSelThreads;
-  const int b0 = tid * per;
-  const int b1 = (b0 + per < n) ? b0 + per : n;
-  int gt = 0, eq = 0;
-  for (int i = b0; i < b1; ++i) {
-    const uint32_t k = skeys[i];
-    gt += (k > thr);
-    eq += (k == thr);
+  // Ordered compaction.  Wave w owns the contiguous range [w0, w1) and walks
+  // it 64 keys at a time (lane-contiguous LDS reads); a key's output position
+  // is (#keys above the threshold before it) + min(#threshold ties before it,
+  // k_eq), both counted with ballots.  Ties are taken lowest position first.
+  const int span = ((n + kSelWaves - 1) / kSelWaves + 63) & ~63;
+  const int w0 = wave * span;
+  const int w1 = (w0 + span < n) ? w0 + span : n;
+  int cgt = 0, ceq = 0;
+  for (int base = w0; base < w1; base += 64) {
+    const int i = base + lane;
+    const uint32_t k = i < w1 ? skeys[i] : 0u;
+    cgt += __popcll(__ballot(i < w1 && k > thr));
+    ceq += __popcll(__ballot(i < w1 && k == thr));
   }
-  const int gt_in = wave_incl_scan(gt, lane);
-  const int eq_in = wave_incl_scan(eq, lane);
-  if (lane == 63) {
-    s_red[wave] = gt_in;
-    s_red[kSelWaves + wave] = eq_in;
+  if (lane == 0) {
+    s_red[wave] = cgt;
+    s_red[kSelWaves + wave] = ceq;
   }
   __syncthreads();
-  int gt_base = 0, eq_base = 0;
-  for (int i = 0; i < wave; ++i) {
-    gt_base += s_red[i];
-    eq_base += s_red[kSelWaves + i];
+  int run_gt = 0, run_eq = 0;
+  for (int v = 0; v < wave; ++v) {
+    run_gt += s_red[v];
+    run_eq += s_red[kSelWaves + v];
   }
-  int eq_rank = eq_base + eq_in - eq;
-  int pos = gt_base + gt_in - gt + (eq_rank < k_eq ? eq_rank : k_eq);
-
-  // ids of this thread's range, fetched together (a later level carries the
-  // ids of the survivors; the first level uses positions)
-  constexpr int kMaxPer = kSelectChunk / kSelThreads;
-  int32_t ids[kMaxPer];
-  {
-    const int32_t *idin = a.ids_in ? a.ids_in + (int64_t)r * a.in_stride + start : nullptr;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int i = b0 + j;
-      ids[j] = (idin && i < b1) ? idin[i] : (int)(start + i);
-    }
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  const int32_t *idin = a.ids_in ? a.ids_in + (int64_t)r * a.in_stride + start : nullptr;
+  int np = 0;
+  if (FINAL && a.map_kind == kMapPool) {
+    np = a.n_pool[r];
+    np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
   }
-  if (FINAL) {
-    int32_t *out = a.out + (int64_t)r * a.k;
-    int np = 0;
-    if (a.map_kind == kMapPool) {
-      np = a.n_pool[r];
-      np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int i = b0 + j;
-      if (i >= b1) break;
-      const uint32_t k = skeys[i];
-      bool take = k > thr;
-      if (k == thr) {
-        take = eq_rank < k_eq;
-        ++eq_rank;
-      }
-      if (take) {
-        int id = ids[j];
+  int32_t *out = FINAL ? a.out + (int64_t)r * a.k : nullptr;
+  uint32_t *kout = FINAL ? nullptr : a.keys_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
+  int32_t *iout = FINAL ? nullptr : a.ids_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
+  for (int base = w0; base < w1; base += 64) {
+    const int i = base + lane;
+    const bool in = i < w1;
+    const uint32_t k = in ? skeys[i] : 0u;
+    const bool gt = in && k > thr;
+    const bool eq = in && k == thr;
+    const unsigned long long bgt = __ballot(gt), beq = __ballot(eq);
+    const int my_gt = run_gt + __popcll(bgt & lt_mask);
+    const int my_eq = run_eq + __popcll(beq & lt_mask);
+    run_gt += __popcll(bgt);
+    run_eq += __popcll(beq);
+    if (gt || (eq && my_eq < k_eq)) {
+      const int pos = my_gt + (my_eq < k_eq ? my_eq : k_eq);
+      int id = idin ? idin[i] : (int)(start + i);
+      if (FINAL) {
         if (a.map_kind == kMapPool) {
           const int p = id >> 3;
           const int b = (p < np) ? a.pool_blocks[(int64_t)r * a.k_blocks + p] : -1;
           id = b * 8 + (id & 7);
         }
-        out[pos++] = id;
+        out[pos] = id;
+      } else {
+        kout[pos] = k;
+        iout[pos] = id;
       }
     }
+  }
+  if (FINAL) {
     for (int i = k_eff + tid; i < a.k; i += kSelThreads) out[i] = -1;
     if (tid == 0) a.n_out[r] = k_eff;
   } else {
-    uint32_t *kout = a.keys_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
-    int32_t *iout = a.ids_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int i = b0 + j;
-      if (i >= b1) break;
-      const uint32_t k = skeys[i];
-      bool take = k > thr;
-      if (k == thr) {
-        take = eq_rank < k_eq;
-        ++eq_rank;
-      }
-      if (take) {
-        kout[pos] = k;
-        iout[pos] = ids[j];
-        ++pos;
-      }
-    }
     for (int i = k_eff + tid; i < a.k; i += kSelThreads) {
       kout[i] = 0u;
       iout[i] = -1;
