@@ -269,22 +269,16 @@ bool swa_ok(const csa2_swa *s) {
          aligned(s->kv, 16);
 }
 
-int32_t attn_max_tiles(int32_t k_pos, int32_t window) {
-  return (k_pos + kAttnTileKeys - 1) / kAttnTileKeys + (window + kAttnTileKeys - 1) / kAttnTileKeys;
-}
-
 // Fills the split fields of `a`; CSA2_E_WORKSPACE if a workspace is given but
 // smaller than the plan needs.
-csa2_status attach_workspace(AttnArgs &a, int32_t n_rows, int32_t n_heads, int32_t max_tiles,
-                             void *workspace, size_t workspace_bytes) {
+csa2_status attach_workspace(AttnArgs &a, int32_t n_rows, int32_t n_heads, int32_t k_pos,
+                             int32_t window, void *workspace, size_t workspace_bytes) {
+  const AttnPlan p = plan_attention(n_rows, n_heads, k_pos, window);
   a.n_split = 1;
-  a.tiles_per_split = max_tiles;
-  if (!workspace) return CSA2_OK;
-  const AttnPlan p = plan_attention(n_rows, n_heads, max_tiles);
-  if (p.n_split <= 1) return CSA2_OK;
+  a.tiles_per_split = p.tiles_per_split;
+  if (!workspace || p.n_split <= 1) return CSA2_OK;
   if (workspace_bytes < p.bytes || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
   a.n_split = p.n_split;
-  a.tiles_per_split = p.tiles_per_split;
   a.part_o = static_cast<float *>(workspace);
   a.part_ml = a.part_o + (size_t)n_rows * p.n_split * n_heads * 512;
   return CSA2_OK;
@@ -402,9 +396,8 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   a.o = o;
   a.lse = lse;
   a.merge_in = 0;
-  const csa2_status ws = attach_workspace(a, n_rows, n_heads,
-                                          attn_max_tiles(k_pos, swa ? swa->window : 0), workspace,
-                                          workspace_bytes);
+  const csa2_status ws = attach_workspace(a, n_rows, n_heads, k_pos, swa ? swa->window : 0,
+                                          workspace, workspace_bytes);
   if (ws != CSA2_OK) return ws;
   if (prepare() != hipSuccess) return CSA2_E_HIP;
   hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
@@ -433,8 +426,8 @@ csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *ro
   a.o = o;
   a.lse = lse;
   a.merge_in = 1;
-  const csa2_status ws = attach_workspace(a, n_rows, n_heads, attn_max_tiles(0, swa->window),
-                                          workspace, workspace_bytes);
+  const csa2_status ws = attach_workspace(a, n_rows, n_heads, 0, swa->window, workspace,
+                                          workspace_bytes);
   if (ws != CSA2_OK) return ws;
   if (prepare() != hipSuccess) return CSA2_E_HIP;
   hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
@@ -446,7 +439,7 @@ size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t k_pos,
   if (n_rows < 0 || (n_heads != 16 && n_heads != 32 && n_heads != 64) || k_pos < 0 ||
       k_pos > kMaxAttnPos || swa_window < 0 || swa_window > 1024)
     return 0;
-  return plan_attention(n_rows, n_heads, attn_max_tiles(k_pos, swa_window)).bytes;
+  return plan_attention(n_rows, n_heads, k_pos, swa_window).bytes;
 }
 
 const char *csa2_status_string(csa2_status status) {

@@ -17,9 +17,10 @@
 //   * Q.K^T: it computes the partial logits over its quarter with 16x16x32
 //     MFMAs (rows = 16 heads, columns = 16 keys); the four partials are summed
 //     through LDS;
-//   * P.V: it writes its dequantised quarter transposed into LDS and
+//   * P.V: it keeps its dequantised quarter in LDS (natural layout) and
 //     accumulates O[:, quarter] with MFMAs (rows = 16 heads, columns = 16
-//     channels, contraction = the 32 keys of the tile).
+//     channels, contraction = the 32 keys of the tile), reading the V
+//     operand back with the hardware transposed LDS read.
 // The softmax is the online (running max) form in base 2; the running max is
 // only raised when a tile's maximum exceeds it by more than 2^8, so most tiles
 // skip the rescale of O.  Probabilities enter the P.V product in f16 and the
@@ -33,7 +34,7 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kTileKeys = kAttnTileKeys;
 constexpr int kMergeSplitLimit = 64;     // splits the merge kernel accepts
-constexpr int kVtStride = 40;          // halves per Vt row (32 keys + pad)
+constexpr int kVnStride = 128 + 16;    // halves per LDS key row: a wave's 128 channels + pad
 constexpr int kPStride = 40;           // halves per P row
 constexpr float kLazyRescale = 8.0f;   // log2 units
 
@@ -53,7 +54,7 @@ attn_kernel(AttnArgs a) {
   constexpr int KPT = kTileKeys / TPH;         // keys per softmax thread
 
   __shared__ __attribute__((aligned(16))) float s_part[4][kTileKeys][H];
-  __shared__ __attribute__((aligned(16))) _Float16 s_vt[512 * kVtStride];
+  __shared__ __attribute__((aligned(16))) _Float16 s_vn[4][kTileKeys * kVnStride];
   __shared__ __attribute__((aligned(16))) _Float16 s_p[H * kPStride];
   __shared__ __attribute__((aligned(16))) float s_alpha[H];
   __shared__ float s_m[H], s_l[H];
@@ -225,14 +226,14 @@ attn_kernel(AttnArgs a) {
         *reinterpret_cast<float4 *>(&s_part[w][16 * kb + c][16 * hb + 4 * G]) =
             make_float4(s[0], s[1], s[2], s[3]);
       }
-    // transposed copy of the dequantised quarter: s_vt[channel][key]
+    // this wave's dequantised quarter, natural layout [key][channel]; the P.V
+    // product reads it back transposed
+    _Float16 *vn = &s_vn[w][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          s_vt[(128 * w + 32 * G + 8 * t + e) * kVtStride + 16 * kb + c] = kf[kb][t][e];
+        *reinterpret_cast<f16x8 *>(vn + (16 * kb + c) * kVnStride + 32 * G + 8 * t) = kf[kb][t];
     __syncthreads();
 
     // online softmax: thread -> head h, keys kk0 .. kk0 + KPT - 1
@@ -289,10 +290,20 @@ attn_kernel(AttnArgs a) {
         }
       }
     }
+    // B operand of channel block db: keys 8G .. 8G+7 at channel 16db + c.
+    // Lane (G, c) addresses row 8G + 4h + c/4, channels 16db + 4 (c % 4) of
+    // the two 4-key halves h.
     f16x8 vb[8];
+    {
+      const _Float16 *r0 = vn + (8 * G + (c >> 2)) * kVnStride + 4 * (c & 3);
+      const _Float16 *r1 = r0 + 4 * kVnStride;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      vb[db] = *reinterpret_cast<const f16x8 *>(&s_vt[(128 * w + 16 * db + c) * kVtStride + 8 * G]);
+      for (int db = 0; db < 8; ++db) {
+        const f16x4 lo = lds_read_tr16(r0 + 16 * db);
+        const f16x4 hi = lds_read_tr16(r1 + 16 * db);
+        vb[db] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const f16x8 pa = *reinterpret_cast<const f16x8 *>(&s_p[(16 * hb + c) * kPStride + 8 * G]);
@@ -439,11 +450,14 @@ attn_merge_kernel(AttnArgs a, int H) {
 
 hipError_t prepare_attention() { return hipSuccess; }
 
-AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t max_tiles) {
+AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t window) {
+  (void)n_heads;
+  const int max_tiles = (k_pos + kTileKeys - 1) / kTileKeys + (window + kTileKeys - 1) / kTileKeys;
   AttnPlan p = {1, max_tiles > 0 ? max_tiles : 1, 0};
   // Few rows leave most of the 256 CUs idle: spread each row's key tiles over
-  // several work-groups (about 384 in all).  Many rows fill the GPU already,
-  // and splitting them would only add partial-result traffic.
+  // several work-groups (about 256 in all, at least two tiles each).  Many rows
+  // fill the GPU already, and splitting them would only add partial-result
+  // traffic.
   if (n_rows >= 192 || max_tiles <= 2) return p;
   int split = (256 + n_rows - 1) / n_rows;
   split = split < max_tiles ? split : max_tiles;

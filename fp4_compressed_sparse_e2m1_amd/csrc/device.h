@@ -102,6 +102,25 @@ __device__ __forceinline__ float from_next_row(float x) {
   return __int_as_float(sw[1]);
 }
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// D = A(16x16) * B(16x16) + C on the matrix cores.  Lane l holds
+// A[l % 16][4*(l/16) .. +3], B[4*(l/16) .. +3][l % 16] and
+// C[4*(l/16) .. +3][l % 16].
+__device__ __forceinline__ f32x4 mfma16x16x16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Transposed LDS read of 16-bit data: within each group of 16 lanes, lane i
+// receives element (i % 4) of the 4-element rows addressed by lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (in that order).
+__device__ __forceinline__ f16x4 lds_read_tr16(const _Float16 *p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
 // D = A(16x32) * B(32x16) + C on the matrix cores.  Lane l holds
 // A[l % 16][8*(l/16) .. +7], B[8*(l/16) .. +7][l % 16] and
 // C[4*(l/16) .. +3][l % 16].

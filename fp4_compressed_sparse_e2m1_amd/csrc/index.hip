@@ -22,10 +22,11 @@
 // accumulate in fp32.
 //
 // Selection: scores are mapped to order-preserving uint32 keys (0 = no
-// candidate).  A work-group loads up to 16,384 keys of one row into LDS and
-// runs a 4-pass 8-bit radix select for the k-th largest key, then an ordered
-// compaction writes the kept positions in ascending order (ties at the
-// threshold go to the lowest positions).  Rows with more keys are cut into
+// candidate).  A work-group holds up to 16,384 keys of one row in registers
+// (32 per thread) and runs an 8-bit radix select for the k-th largest key,
+// starting at the highest bit in which its keys differ, with LDS histograms;
+// an ordered compaction (ballot prefix counts) then writes the kept positions
+// in ascending order, ties at the threshold going to the lowest positions.  Rows with more keys are cut into
 // chunks whose Top-k survivors feed a further level, which keeps the result
 // exact because a global Top-k element is in its chunk's Top-k.
 #include "device.h"
@@ -158,13 +159,21 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-template <bool FINAL>
+// Keys per thread: a work-group of 512 threads holds one chunk of up to
+// kSelectChunk keys in registers.  Thread (wave w, lane l) holds positions
+// w * kSelSpan + 64 j + l, j < kKeysPerThread, so every wave owns a contiguous
+// range and every load is lane-contiguous.
+constexpr int kKeysPerThread = kSelectChunk / kSelThreads;
+constexpr int kSelSpan = 64 * kKeysPerThread;
+
+template <bool FINAL, bool IDS>
 __global__ void __launch_bounds__(kSelThreads)
 select_kernel(SelectArgs a) {
-  extern __shared__ uint32_t skeys[];
   __shared__ uint32_t hist[256];
+  __shared__ int32_t s_pool[FINAL ? kMaxPoolBlocks : 1];
   __shared__ int s_red[kSelWaves * 2];
-  __shared__ int s_digit, s_above, s_nvalid;
+  __shared__ uint32_t s_min[kSelWaves], s_max[kSelWaves];
+  __shared__ int s_digit, s_above;
 
   const int r = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -186,113 +195,138 @@ select_kernel(SelectArgs a) {
   int n = (int)((int64_t)n_row - start);
   n = n < 0 ? 0 : (n > kSelectChunk ? kSelectChunk : n);
 
-  // load keys (all loads of a thread in flight at once), count the valid
-  // (non-zero) ones
+  // keys into registers; count the valid (non-zero) ones, their min and max
   const uint32_t *kin = a.keys_in + (int64_t)r * a.in_stride + start;
+  const int base = wave * kSelSpan + lane;
+  uint32_t key[kKeysPerThread];
+#pragma unroll
+  for (int j = 0; j < kKeysPerThread; ++j) {
+    const int i = base + 64 * j;
+    key[j] = i < n ? kin[i] : 0u;
+  }
+  // ids carried from an earlier level, fetched with the keys
+  int32_t ids[IDS ? kKeysPerThread : 1];
+  if (IDS) {
+    const int32_t *idin = a.ids_in + (int64_t)r * a.in_stride + start;
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+      const int i = base + 64 * j;
+      ids[j] = i < n ? idin[i] : -1;
+    }
+  }
+  // the pool row, for mapping candidate slots to entries
+  int np = 0;
+  if (FINAL && a.map_kind == kMapPool) {
+    np = a.n_pool[r];
+    np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
+    for (int i = tid; i < np; i += kSelThreads) s_pool[i] = a.pool_blocks[(int64_t)r * a.k_blocks + i];
+  }
   int nvalid = 0;
-  {
-    constexpr int PER = kSelectChunk / kSelThreads;
-    uint32_t v[PER];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = j * kSelThreads + tid;
-      v[j] = i < n ? kin[i] : 0u;
-    }
+  for (int j = 0; j < kKeysPerThread; ++j) {
+    nvalid += key[j] != 0u;
+    if (key[j] != 0u) kmin = kmin < key[j] ? kmin : key[j];
+    kmax = kmax > key[j] ? kmax : key[j];
+  }
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = j * kSelThreads + tid;
-      if (i < n) skeys[i] = v[j];
-      nvalid += (v[j] != 0u);
-    }
+  for (int off = 32; off > 0; off >>= 1) {
+    nvalid += __shfl_xor(nvalid, off);
+    const uint32_t om = __shfl_xor(kmin, off), oM = __shfl_xor(kmax, off);
+    kmin = kmin < om ? kmin : om;
+    kmax = kmax > oM ? kmax : oM;
+  }
+  if (lane == 0) {
+    s_red[wave] = nvalid;
+    s_min[wave] = kmin;
+    s_max[wave] = kmax;
   }
   if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  nvalid = 0;
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) nvalid += __shfl_xor(nvalid, off);
-  if (lane == 0) s_red[wave] = nvalid;
-  __syncthreads();
-  if (tid == 0) {
-    int t = 0;
-    for (int i = 0; i < kSelWaves; ++i) t += s_red[i];
-    s_nvalid = t;
+  for (int v = 0; v < kSelWaves; ++v) {
+    nvalid += s_red[v];
+    kmin = kmin < s_min[v] ? kmin : s_min[v];
+    kmax = kmax > s_max[v] ? kmax : s_max[v];
   }
-  __syncthreads();
-  nvalid = s_nvalid;
   const int k_eff = nvalid < a.k ? nvalid : a.k;
 
-  // radix select of the k_eff-th largest key
+  // Radix select of the k_eff-th largest key.  Bits above the highest bit in
+  // which the smallest and largest valid keys differ are common to all valid
+  // keys, so the digits start there (8 bits per pass).
   uint32_t thr = 0u;
   int k_eq = 0;
   if (k_eff < nvalid) {
-    uint32_t prefix = 0u, mask = 0u;
-    int k_rem = k_eff;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      // Histogram of the current digit over keys that match the prefix.  Most
-      // keys share a few leading digits, so lanes holding the same bin as the
-      // wave's first active lane add their count with one atomic.
-      for (int base = wave * 64; base < n; base += kSelThreads) {
-        const int i = base + lane;
-        const uint32_t k = i < n ? skeys[i] : 0u;
-        const bool m = i < n && (k & mask) == prefix;
-        const uint32_t bin = (k >> shift) & 255u;
-        const unsigned long long act = __ballot(m);
-        if (act) {
-          const int leader = __ffsll((long long)act) - 1;
-          const uint32_t lb = __shfl(bin, leader);
-          const unsigned long long same = __ballot(m && bin == lb);
-          if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
-          if (m && bin != lb) atomicAdd(&hist[bin], 1u);
-        }
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 255-4l .. 252-4l (descending)
-        int cnt[4];
-        int local = 0;
+    const uint32_t diff = kmin ^ kmax;
+    if (diff == 0u) {
+      thr = kmin;
+      k_eq = k_eff;
+    } else {
+      const int hb = 31 - __clz(diff);
+      uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
+      uint32_t prefix = kmin & mask;
+      int k_rem = k_eff;
+      for (int top = hb; top >= 0; top -= 8) {
+        const int shift = top >= 7 ? top - 7 : 0;
+        const uint32_t dmask = (2u << (top - shift)) - 1u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          cnt[j] = (int)hist[255 - 4 * lane - j];
-          local += cnt[j];
-        }
-        const int incl = wave_incl_scan(local, lane);
-        const int excl = incl - local;
-        if (excl < k_rem && k_rem <= incl) {
-          int cum = excl;
+        for (int j = 0; j < kKeysPerThread; ++j)
+          if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+        __syncthreads();
+        if (wave == 0) {
+          // lane l owns bins 255-4l .. 252-4l (descending)
+          int cnt[4];
+          int local = 0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            if (cum + cnt[j] >= k_rem) {
-              s_digit = 255 - 4 * lane - j;
-              s_above = cum;
-              break;
+            cnt[j] = (int)hist[255 - 4 * lane - j];
+            local += cnt[j];
+          }
+          const int incl = wave_incl_scan(local, lane);
+          const int excl = incl - local;
+          if (excl < k_rem && k_rem <= incl) {
+            int cum = excl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (cum + cnt[j] >= k_rem) {
+                s_digit = 255 - 4 * lane - j;
+                s_above = cum;
+                break;
+              }
+              cum += cnt[j];
             }
-            cum += cnt[j];
           }
         }
+        __syncthreads();
+        prefix |= (uint32_t)s_digit << shift;
+        mask |= dmask << shift;
+        k_rem -= s_above;
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
       }
-      __syncthreads();
-      prefix |= (uint32_t)s_digit << shift;
-      mask |= 255u << shift;
-      k_rem -= s_above;
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
+      thr = prefix;
+      k_eq = k_rem;
     }
-    thr = prefix;
-    k_eq = k_rem;
   }
 
-  // Ordered compaction.  Wave w owns the contiguous range [w0, w1) and walks
-  // it 64 keys at a time (lane-contiguous LDS reads); a key's output position
-  // is (#keys above the threshold before it) + min(#threshold ties before it,
-  // k_eq), both counted with ballots.  Ties are taken lowest position first.
-  const int span = ((n + kSelWaves - 1) / kSelWaves + 63) & ~63;
-  const int w0 = wave * span;
-  const int w1 = (w0 + span < n) ? w0 + span : n;
+  // Ordered compaction from registers: a key's output position is (#keys
+  // above the threshold before it) + min(#threshold ties before it, k_eq),
+  // counted with ballots; ties are taken lowest position first.
   int cgt = 0, ceq = 0;
-  for (int base = w0; base < w1; base += 64) {
-    const int i = base + lane;
-    const uint32_t k = i < w1 ? skeys[i] : 0u;
-    cgt += __popcll(__ballot(i < w1 && k > thr));
-    ceq += __popcll(__ballot(i < w1 && k == thr));
+#pragma unroll
+  for (int j = 0; j < kKeysPerThread; ++j) {
+    cgt += key[j] > thr;
+    ceq += (key[j] == thr) && (base + 64 * j < n);
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    cgt += __shfl_xor(cgt, off);
+    ceq += __shfl_xor(ceq, off);
+  }
+  __syncthreads();
   if (lane == 0) {
     s_red[wave] = cgt;
     s_red[kSelWaves + wave] = ceq;
@@ -304,21 +338,15 @@ select_kernel(SelectArgs a) {
     run_eq += s_red[kSelWaves + v];
   }
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  const int32_t *idin = a.ids_in ? a.ids_in + (int64_t)r * a.in_stride + start : nullptr;
-  int np = 0;
-  if (FINAL && a.map_kind == kMapPool) {
-    np = a.n_pool[r];
-    np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
-  }
   int32_t *out = FINAL ? a.out + (int64_t)r * a.k : nullptr;
   uint32_t *kout = FINAL ? nullptr : a.keys_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
   int32_t *iout = FINAL ? nullptr : a.ids_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
-  for (int base = w0; base < w1; base += 64) {
-    const int i = base + lane;
-    const bool in = i < w1;
-    const uint32_t k = in ? skeys[i] : 0u;
-    const bool gt = in && k > thr;
-    const bool eq = in && k == thr;
+#pragma unroll
+  for (int j = 0; j < kKeysPerThread; ++j) {
+    const int i = base + 64 * j;
+    const uint32_t k = key[j];
+    const bool gt = k > thr;
+    const bool eq = (k == thr) && i < n;
     const unsigned long long bgt = __ballot(gt), beq = __ballot(eq);
     const int my_gt = run_gt + __popcll(bgt & lt_mask);
     const int my_eq = run_eq + __popcll(beq & lt_mask);
@@ -326,11 +354,11 @@ select_kernel(SelectArgs a) {
     run_eq += __popcll(beq);
     if (gt || (eq && my_eq < k_eq)) {
       const int pos = my_gt + (my_eq < k_eq ? my_eq : k_eq);
-      int id = idin ? idin[i] : (int)(start + i);
+      int id = IDS ? ids[j] : (int)(start + i);
       if (FINAL) {
         if (a.map_kind == kMapPool) {
           const int p = id >> 3;
-          const int b = (p < np) ? a.pool_blocks[(int64_t)r * a.k_blocks + p] : -1;
+          const int b = (p < np) ? s_pool[p] : -1;
           id = b * 8 + (id & 7);
         }
         out[pos] = id;
@@ -367,24 +395,24 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int6
   return hipGetLastError();
 }
 
-hipError_t prepare_select() {
-  const int bytes = kSelectChunk * (int)sizeof(uint32_t);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<false>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
+hipError_t prepare_select() { return hipSuccess; }
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
                          hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   dim3 grid((unsigned)n_chunks, (unsigned)n_rows);
-  const size_t lds = (size_t)kSelectChunk * sizeof(uint32_t);
-  if (final_level)
-    select_kernel<true><<<grid, kSelThreads, lds, stream>>>(a);
-  else
-    select_kernel<false><<<grid, kSelThreads, lds, stream>>>(a);
+  const bool ids = a.ids_in != nullptr;
+  if (final_level) {
+    if (ids)
+      select_kernel<true, true><<<grid, kSelThreads, 0, stream>>>(a);
+    else
+      select_kernel<true, false><<<grid, kSelThreads, 0, stream>>>(a);
+  } else {
+    if (ids)
+      select_kernel<false, true><<<grid, kSelThreads, 0, stream>>>(a);
+    else
+      select_kernel<false, false><<<grid, kSelThreads, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -61,8 +61,10 @@ struct SelectArgs {
   int32_t k_blocks;
 };
 
-// Keys held in LDS by one selection work-group.
+// Keys held by one selection work-group (32 per thread), and the largest pool
+// (in blocks) a selection maps through.
 constexpr int kSelectChunk = 16384;
+constexpr int kMaxPoolBlocks = 4096;
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
                          hipStream_t stream);
@@ -87,10 +89,10 @@ struct AttnArgs {
   float *o;                   // [R][H][512]
   float *lse;                 // [R][H]
   int32_t merge_in;           // 1: start from (o, lse) as an earlier result
-  // split of a row's key tiles over several work-groups (n_split > 1):
+  // split of a row's keys over several work-groups (n_split > 1):
   // unnormalised partial results, merged by a second kernel
   int32_t n_split;
-  int32_t tiles_per_split;
+  int32_t tiles_per_split;    // key tiles (32 keys; 16-key blocks for 16 heads) per work-group
   float *part_o;              // [R][n_split][H][512]
   float *part_ml;             // [R][n_split][H][2]  (running max in log2 units, sum)
 };
@@ -105,7 +107,7 @@ struct AttnPlan {
   int32_t tiles_per_split;
   size_t bytes;
 };
-AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t max_tiles);
+AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t window);
 
 hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, hipStream_t stream);
 hipError_t prepare_attention();

@@ -144,11 +144,14 @@ def test_attention_validation():
     assert m(FAKE, 20, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == UNSUPPORTED
     assert m(FAKE, 16, FAKE, 0, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == OK
     # a split needs its workspace: given but too small is an error, NULL is not
-    ws = lib.csa2_attn_workspace_size(8, 16, 512, 128)
-    assert ws >= 8 * 2 * 16 * 514 * 4
+    ws = lib.csa2_attn_workspace_size(8, 64, 512, 128)
+    assert ws >= 8 * 2 * 64 * 514 * 4
+    assert lib.csa2_attn_workspace_size(8, 16, 512, 128) >= 8 * 10 * 16 * 514 * 4  # 20 tiles -> 10 parts
+    assert lib.csa2_attn_workspace_size(256, 16, 512, 128) == 0      # 16 heads, many rows: no split
     assert lib.csa2_attn_workspace_size(256, 64, 512, 128) == 0      # many rows: no split
     assert lib.csa2_attn_workspace_size(8, 24, 512, 128) == 0        # invalid heads
     a = list(base)
+    a[2] = 64
     a[12], a[13] = FAKE, 64                                           # split planned, 64 B given
     assert f(*a) == WORKSPACE
     a[12] = FAKE + 8

@@ -274,7 +274,7 @@ def test_sparse_attn_global_fused_and_merge(csa2, H, split):
     ws_g = csa2.attn_workspace(R, H, k_pos, 0) if split else None
     ws_m = csa2.attn_workspace(R, H, 0, 128) if split else None
     ws_f = csa2.attn_workspace(R, H, k_pos, 128) if split else None
-    if split:
+    if split and H > 16:       # 16 heads split keys inside one work-group and need none
         assert ws_g is not None and ws_m is not None and ws_f is not None
     # global branch only
     o = torch.empty((R, H, 512), device="cuda")
