@@ -14,10 +14,15 @@ with its own 16-head query and its own 128-row FP8 SWA window
 Inputs are seeded synthetic tensors already resident in HBM; the cache
 (8 x 1M entries x 356 B) is built before timing.
 
+The timed steps launch every kernel from Python (the GPU, not the host, is
+the limit: replaying the step as HIP graphs measured no faster); --graph
+replays it as three HIP graphs (the append, the scan, everything after it),
+after checking that a replay reproduces the eager step's outputs bit for bit.
+
 Output: one JSON line.  value = query tokens per second per CSA2 layer
 (= batch x layers / step time); roofline = the Full-layer scan kernel,
-timed with HIP events on the stream it runs on; cpu_baseline = the oracle
-on a bounded sample of the same step.
+timed with HIP events recorded between the graph launches on the stream
+they run on; cpu_baseline = the oracle on a bounded sample of the same step.
 """
 import argparse
 import json
@@ -44,6 +49,8 @@ def parse():
                     help="query rows of the step the oracle runs for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ctx", type=int, default=None, help="override the context (testing only)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as HIP graphs instead of launching every kernel from Python")
     return ap.parse_args()
 
 
@@ -96,61 +103,145 @@ def build(ctx_override=None):
     return ctx
 
 
-def step(c, ev=None):
-    """One decode step of the 20-layer stack.  ev: optional list of event
-    pairs to record (scan start/end, then one boundary after every layer)."""
+def _append(c):
+    csa2, cache = c["csa2"], c["cache"]
+    csa2.csa2_quantize_fp4(c["new_lat"], 16, cache.kv_codes, cache.kv_scales, dst_rows=c["new_dst"])
+    csa2.csa2_quantize_fp4(c["new_ik"], 32, cache.ik_codes, cache.ik_scales, dst_rows=c["new_dst"])
+
+
+def _scan(c, l):
+    c["csa2"].csa2_index_scan(c["cache"], c["q_idx"][l], c["w"][l], c["row_seq"], c["row_nvis"], c["T"],
+                              c["block_keys"])
+
+
+def _layer_tail(c, l, mode, src):
+    """Everything of layer l after the scan; returns the layer whose Top-512
+    later Reuse layers attend over."""
     csa2, wl, T = c["csa2"], c["wl"], c["T"]
     cache, seqs, nvis = c["cache"], c["row_seq"], c["row_nvis"]
+    if mode == "full":
+        csa2.csa2_index_pool(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["block_keys"],
+                             wl.k_blk, wl.k_pos, c["pool"], c["n_pool"], c["topk"][l],
+                             c["n_topk"][l], c["ws_pool"])
+        src = l
+    elif mode == "reindex":
+        csa2.csa2_index_reindex(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["pool"],
+                                c["n_pool"], wl.k_blk, wl.k_pos, c["topk"][l], c["n_topk"][l],
+                                c["ws_re"])
+        src = l
+    csa2.csa2_sparse_attn(cache, c["q"][l], seqs, c["topk"][src], c["n_topk"][src], SCALE,
+                          c["o"], c["lse"], swa=c["swa"][l], workspace=c["ws_attn"])
+    return src
+
+
+def step(c, ev=None):
+    """One decode step of the 20-layer stack, every kernel launched from
+    Python.  ev: optional events to record (scan start/end, then one boundary
+    after every layer)."""
     src = None
-    for l, mode in enumerate(wl.layers):
+    for l, mode in enumerate(c["wl"].layers):
         if mode == "full":
-            csa2.csa2_quantize_fp4(c["new_lat"], 16, cache.kv_codes, cache.kv_scales, dst_rows=c["new_dst"])
-            csa2.csa2_quantize_fp4(c["new_ik"], 32, cache.ik_codes, cache.ik_scales, dst_rows=c["new_dst"])
+            _append(c)
             if ev is not None:
                 ev["scan0"].record()
-            csa2.csa2_index_scan(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["block_keys"])
+            _scan(c, l)
             if ev is not None:
                 ev["scan1"].record()
-            csa2.csa2_index_pool(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["block_keys"],
-                                 wl.k_blk, wl.k_pos, c["pool"], c["n_pool"], c["topk"][l],
-                                 c["n_topk"][l], c["ws_pool"])
-            src = l
-        elif mode == "reindex":
-            csa2.csa2_index_reindex(cache, c["q_idx"][l], c["w"][l], seqs, nvis, T, c["pool"],
-                                    c["n_pool"], wl.k_blk, wl.k_pos, c["topk"][l], c["n_topk"][l],
-                                    c["ws_re"])
-            src = l
-        csa2.csa2_sparse_attn(cache, c["q"][l], seqs, c["topk"][src], c["n_topk"][src], SCALE,
-                              c["o"], c["lse"], swa=c["swa"][l], workspace=c["ws_attn"])
+        src = _layer_tail(c, l, mode, src)
         if ev is not None:
             ev["layer"][l].record()
 
 
-def run_gpu(c, steps, warmup):
+def capture(c):
+    """The step as three HIP graphs: the append, the Full layer's scan, and
+    everything after it (the stack opens with its one Full layer)."""
+    import torch
+
+    layers = c["wl"].layers
+    assert layers[0] == "full" and "full" not in layers[1:]
+
+    def rest():
+        src = None
+        for l, mode in enumerate(layers):
+            src = _layer_tail(c, l, mode, src)
+
+    graphs = []
+    for fn in (lambda: _append(c), lambda: _scan(c, 0), rest):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def _outputs(c):
+    """Copies of what a step writes: the selections of the Full and Reindex
+    layers, the pool, and the last layer's attention output."""
+    sel = [l for l, m in enumerate(c["wl"].layers) if m != "reuse"]
+    return [t.clone() for t in [c["topk"][l] for l in sel] + [c["n_topk"][l] for l in sel]
+            + [c["pool"], c["n_pool"], c["o"], c["lse"]]]
+
+
+def run_gpu(c, steps, warmup, eager):
+    """Times `steps` steps after `warmup` untimed ones.  Returns the wall time,
+    the scan kernel's mean event time (ms), and the per-layer event times (ms)
+    of a separate eager pass."""
     import torch
 
     for _ in range(warmup):
         step(c)
     torch.cuda.synchronize()
     L = c["L"]
+    # per-layer breakdown: eager launches with events after every layer (untimed)
     evs = [dict(scan0=torch.cuda.Event(enable_timing=True), scan1=torch.cuda.Event(enable_timing=True),
                 start=torch.cuda.Event(enable_timing=True),
-                layer=[torch.cuda.Event(enable_timing=True) for _ in range(L)]) for _ in range(steps)]
+                layer=[torch.cuda.Event(enable_timing=True) for _ in range(L)]) for _ in range(3)]
+    for e in evs:
+        e["start"].record()
+        step(c, e)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(steps):
-        evs[k]["start"].record()
-        step(c, evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    scan_ms = sum(e["scan0"].elapsed_time(e["scan1"]) for e in evs) / steps
     per_layer = [0.0] * L
     for e in evs:
         prev = e["start"]
         for l in range(L):
-            per_layer[l] += prev.elapsed_time(e["layer"][l]) / steps
+            per_layer[l] += prev.elapsed_time(e["layer"][l]) / len(evs)
             prev = e["layer"][l]
+    ref = _outputs(c)
+    graphs = None
+    if not eager:
+        graphs = capture(c)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, _outputs(c)):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay differs from the eager step")
+        for _ in range(warmup):
+            for g in graphs:
+                g.replay()
+    scan = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        if graphs is None:
+            step(c, dict(scan0=scan[k][0], scan1=scan[k][1], layer=[_NoEvent] * L))
+        else:
+            graphs[0].replay()
+            scan[k][0].record()
+            graphs[1].replay()
+            scan[k][1].record()
+            graphs[2].replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = sum(a.elapsed_time(b) for a, b in scan) / steps
     return wall, scan_ms, per_layer
+
+
+class _NoEvent:
+    @staticmethod
+    def record():
+        pass
 
 
 def cpu_baseline(c, rows):
@@ -252,7 +343,7 @@ def main():
     t_build = time.perf_counter()
     c = build(args.ctx)
     t_build = time.perf_counter() - t_build
-    wall, scan_ms, per_layer = run_gpu(c, args.steps, args.warmup)
+    wall, scan_ms, per_layer = run_gpu(c, args.steps, args.warmup, not args.graph)
     B, T, L = c["B"], c["T"], c["L"]
     ms_step = wall * 1e3 / args.steps
     value = B * L / (wall / args.steps)
@@ -277,12 +368,13 @@ def main():
         "config": {"workload": c["wl"].name, "batch": B, "context_entries": T, "layers": L,
                    "layer_modes": {"full": 1, "reindex": 4, "reuse": 15}, "heads": c["H"],
                    "k_blocks": c["wl"].k_blk, "k_pos": c["wl"].k_pos, "swa": c["wl"].swa,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "launch": "HIP graph replay (append, scan, rest)" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "kernel": "score_kernel<block max> (csa2_index_scan)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(scan_ms * 1e3, 2)},
-        "per_layer_us": {k: round(v, 2) for k, v in mode_us.items()},
+        "per_layer_us_eager": {k: round(v, 2) for k, v in mode_us.items()},
         "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
         "build_s": round(t_build, 1),
     }

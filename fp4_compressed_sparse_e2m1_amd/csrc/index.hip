@@ -23,9 +23,10 @@
 //
 // Selection: scores are mapped to order-preserving uint32 keys (0 = no
 // candidate).  A work-group holds up to 16,384 keys of one row in registers
-// (32 per thread) and runs an 8-bit radix select for the k-th largest key,
+// (16 per thread) and runs an 8-bit radix select for the k-th largest key,
 // starting at the highest bit in which its keys differ, with LDS histograms;
-// an ordered compaction (ballot prefix counts) then writes the kept positions
+// once the keys still in play fit in LDS, one wave finishes the digits alone.
+// An ordered compaction (ballot prefix counts) then writes the kept positions
 // in ascending order, ties at the threshold going to the lowest positions.  Rows with more keys are cut into
 // chunks whose Top-k survivors feed a further level, which keeps the result
 // exact because a global Top-k element is in its chunk's Top-k.
@@ -147,8 +148,30 @@ score_kernel(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------- selection
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+// Keys per thread: a work-group holds one chunk of up to kSelectChunk keys in
+// registers.  Thread (wave w, lane l) holds positions w * kSelSpan + 64 j + l,
+// j < kKeysPerThread, so every wave owns a contiguous range and every load is
+// lane-contiguous.
+constexpr int kKeysPerThread = kSelectChunk / kSelThreads;
+constexpr int kSelSpan = 64 * kKeysPerThread;
+// Keys left after the first radix digit that one wave finishes alone.
+constexpr int kCandCap = 4096;
+
+// Reductions over the 64 lanes of a wave (DPP inside 16-lane rows, then the
+// row swaps); every lane receives the result.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, int lane, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppXor1, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppXor2, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppHalfMirror, 0xF, 0xF, false));
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppRowRor8, 0xF, 0xF, false));
+  const auto s16 = __builtin_amdgcn_permlane16_swap((int)x, (int)x, false, false);
+  x = op(x, (uint32_t)(((lane >> 4) & 1) ? s16[0] : s16[1]));
+  const auto s32 = __builtin_amdgcn_permlane32_swap((int)x, (int)x, false, false);
+  return op(x, (uint32_t)(lane < 32 ? s32[1] : s32[0]));
+}
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
@@ -159,21 +182,56 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Keys per thread: a work-group of 512 threads holds one chunk of up to
-// kSelectChunk keys in registers.  Thread (wave w, lane l) holds positions
-// w * kSelSpan + 64 j + l, j < kKeysPerThread, so every wave owns a contiguous
-// range and every load is lane-contiguous.
-constexpr int kKeysPerThread = kSelectChunk / kSelThreads;
-constexpr int kSelSpan = 64 * kKeysPerThread;
+// Orders the LDS accesses of one wave before and after it (no work-group
+// barrier: the other waves are not involved).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave finds the bin of a 256-bin histogram that holds the k_rem-th
+// largest key (bins scanned from the top); returns the bin and, through
+// *above, the number of keys in higher bins.
+__device__ __forceinline__ int find_digit(const uint32_t *hist, int k_rem, int lane, int *above) {
+  int cnt[4];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    cnt[j] = (int)hist[255 - 4 * lane - j];
+    local += cnt[j];
+  }
+  const int incl = wave_incl_scan(local, lane);
+  const int excl = incl - local;
+  int digit = -1, abv = 0;
+  if (excl < k_rem && k_rem <= incl) {
+    int cum = excl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (digit < 0 && cum + cnt[j] >= k_rem) {
+        digit = 255 - 4 * lane - j;
+        abv = cum;
+      }
+      cum += cnt[j];
+    }
+  }
+  const unsigned long long owner = __ballot(digit >= 0);
+  const int src = __ffsll((long long)owner) - 1;
+  *above = __shfl(abv, src);
+  return __shfl(digit, src);
+}
 
 template <bool FINAL, bool IDS>
 __global__ void __launch_bounds__(kSelThreads)
 select_kernel(SelectArgs a) {
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_cand[kCandCap];
   __shared__ int32_t s_pool[FINAL ? kMaxPoolBlocks : 1];
   __shared__ int s_red[kSelWaves * 2];
   __shared__ uint32_t s_min[kSelWaves], s_max[kSelWaves];
-  __shared__ int s_digit, s_above;
+  __shared__ int s_digit, s_above, s_ncand;
+  __shared__ uint32_t s_thr;
+  __shared__ int s_keq;
 
   const int r = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -195,7 +253,7 @@ select_kernel(SelectArgs a) {
   int n = (int)((int64_t)n_row - start);
   n = n < 0 ? 0 : (n > kSelectChunk ? kSelectChunk : n);
 
-  // keys into registers; count the valid (non-zero) ones, their min and max
+  // keys (and carried ids) into registers
   const uint32_t *kin = a.keys_in + (int64_t)r * a.in_stride + start;
   const int base = wave * kSelSpan + lane;
   uint32_t key[kKeysPerThread];
@@ -204,7 +262,6 @@ select_kernel(SelectArgs a) {
     const int i = base + 64 * j;
     key[j] = i < n ? kin[i] : 0u;
   }
-  // ids carried from an earlier level, fetched with the keys
   int32_t ids[IDS ? kKeysPerThread : 1];
   if (IDS) {
     const int32_t *idin = a.ids_in + (int64_t)r * a.in_stride + start;
@@ -221,45 +278,43 @@ select_kernel(SelectArgs a) {
     np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
     for (int i = tid; i < np; i += kSelThreads) s_pool[i] = a.pool_blocks[(int64_t)r * a.k_blocks + i];
   }
-  int nvalid = 0;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  // count, min and max of the valid (non-zero) keys
+  uint32_t nvalid = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < kKeysPerThread; ++j) {
     nvalid += key[j] != 0u;
     if (key[j] != 0u) kmin = kmin < key[j] ? kmin : key[j];
     kmax = kmax > key[j] ? kmax : key[j];
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    nvalid += __shfl_xor(nvalid, off);
-    const uint32_t om = __shfl_xor(kmin, off), oM = __shfl_xor(kmax, off);
-    kmin = kmin < om ? kmin : om;
-    kmax = kmax > oM ? kmax : oM;
-  }
+  nvalid = wave_reduce(nvalid, lane, [](uint32_t x, uint32_t y) { return x + y; });
+  kmin = wave_reduce(kmin, lane, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+  kmax = wave_reduce(kmax, lane, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
   if (lane == 0) {
-    s_red[wave] = nvalid;
+    s_red[wave] = (int)nvalid;
     s_min[wave] = kmin;
     s_max[wave] = kmax;
   }
   if (tid < 256) hist[tid] = 0;
+  if (tid == 0) s_ncand = 0;
   __syncthreads();
-  nvalid = 0;
+  int nv_all = 0;
   kmin = 0xFFFFFFFFu;
   kmax = 0u;
 #pragma unroll
   for (int v = 0; v < kSelWaves; ++v) {
-    nvalid += s_red[v];
+    nv_all += s_red[v];
     kmin = kmin < s_min[v] ? kmin : s_min[v];
     kmax = kmax > s_max[v] ? kmax : s_max[v];
   }
-  const int k_eff = nvalid < a.k ? nvalid : a.k;
+  const int k_eff = nv_all < a.k ? nv_all : a.k;
 
   // Radix select of the k_eff-th largest key.  Bits above the highest bit in
   // which the smallest and largest valid keys differ are common to all valid
-  // keys, so the digits start there (8 bits per pass).
+  // keys, so the 8-bit digits start there.  After the first digit the keys
+  // still in play are usually few: one wave gathers them and finishes alone.
   uint32_t thr = 0u;
   int k_eq = 0;
-  if (k_eff < nvalid) {
+  if (k_eff < nv_all) {
     const uint32_t diff = kmin ^ kmax;
     if (diff == 0u) {
       thr = kmin;
@@ -269,7 +324,9 @@ select_kernel(SelectArgs a) {
       uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
       uint32_t prefix = kmin & mask;
       int k_rem = k_eff;
-      for (int top = hb; top >= 0; top -= 8) {
+      int top = hb;
+      bool wave_path = false;
+      while (top >= 0 && !wave_path) {
         const int shift = top >= 7 ? top - 7 : 0;
         const uint32_t dmask = (2u << (top - shift)) - 1u;
 #pragma unroll
@@ -277,59 +334,93 @@ select_kernel(SelectArgs a) {
           if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
         __syncthreads();
         if (wave == 0) {
-          // lane l owns bins 255-4l .. 252-4l (descending)
-          int cnt[4];
-          int local = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            cnt[j] = (int)hist[255 - 4 * lane - j];
-            local += cnt[j];
-          }
-          const int incl = wave_incl_scan(local, lane);
-          const int excl = incl - local;
-          if (excl < k_rem && k_rem <= incl) {
-            int cum = excl;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (cum + cnt[j] >= k_rem) {
-                s_digit = 255 - 4 * lane - j;
-                s_above = cum;
-                break;
-              }
-              cum += cnt[j];
-            }
+          int above;
+          const int d = find_digit(hist, k_rem, lane, &above);
+          if (lane == 0) {
+            s_digit = d;
+            s_above = above;
+            s_ncand = (int)hist[d];
           }
         }
         __syncthreads();
         prefix |= (uint32_t)s_digit << shift;
         mask |= dmask << shift;
         k_rem -= s_above;
+        const int ncand = s_ncand;
+        top = shift - 1;
+        __syncthreads();
         if (tid < 256) hist[tid] = 0;
+        if (top >= 0 && ncand <= kCandCap) {
+          // gather the keys still in play
+          if (tid == 0) s_ncand = 0;
+          __syncthreads();
+          const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+          for (int j = 0; j < kKeysPerThread; ++j) {
+            const bool m = key[j] != 0u && (key[j] & mask) == prefix;
+            const unsigned long long bm = __ballot(m);
+            if (bm) {
+              int off = 0;
+              if (lane == 0) off = atomicAdd(&s_ncand, __popcll(bm));
+              off = __shfl(off, 0);
+              if (m) s_cand[off + __popcll(bm & lt)] = key[j];
+            }
+          }
+          wave_path = true;
+        }
         __syncthreads();
       }
-      thr = prefix;
-      k_eq = k_rem;
+      if (wave_path) {
+        if (wave == 0) {
+          const int ncand = s_ncand;
+          while (top >= 0) {
+            const int shift = top >= 7 ? top - 7 : 0;
+            const uint32_t dmask = (2u << (top - shift)) - 1u;
+            for (int i = lane; i < ncand; i += 64) {
+              const uint32_t k = s_cand[i];
+              if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+            }
+            wave_sync();
+            int above;
+            const int d = find_digit(hist, k_rem, lane, &above);
+            prefix |= (uint32_t)d << shift;
+            mask |= dmask << shift;
+            k_rem -= above;
+            wave_sync();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
+            wave_sync();
+            top = shift - 1;
+          }
+          if (lane == 0) {
+            s_thr = prefix;
+            s_keq = k_rem;
+          }
+        }
+        __syncthreads();
+        thr = s_thr;
+        k_eq = s_keq;
+      } else {
+        thr = prefix;
+        k_eq = k_rem;
+      }
     }
   }
 
   // Ordered compaction from registers: a key's output position is (#keys
   // above the threshold before it) + min(#threshold ties before it, k_eq),
   // counted with ballots; ties are taken lowest position first.
-  int cgt = 0, ceq = 0;
+  uint32_t cgt = 0, ceq = 0;
 #pragma unroll
   for (int j = 0; j < kKeysPerThread; ++j) {
     cgt += key[j] > thr;
     ceq += (key[j] == thr) && (base + 64 * j < n);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    cgt += __shfl_xor(cgt, off);
-    ceq += __shfl_xor(ceq, off);
-  }
-  __syncthreads();
+  cgt = wave_reduce(cgt, lane, [](uint32_t x, uint32_t y) { return x + y; });
+  ceq = wave_reduce(ceq, lane, [](uint32_t x, uint32_t y) { return x + y; });
   if (lane == 0) {
-    s_red[wave] = cgt;
-    s_red[kSelWaves + wave] = ceq;
+    s_red[wave] = (int)cgt;
+    s_red[kSelWaves + wave] = (int)ceq;
   }
   __syncthreads();
   int run_gt = 0, run_eq = 0;
