@@ -45,6 +45,25 @@ struct RawTile {
   bool valid[2];
 };
 
+// Max / sum over each aligned group of N lanes (N = 2, 4, 8 or 16: a quad,
+// half row or row of the DPP network), in every lane of the group.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+  if (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  if (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if (N >= 16) x = fmaxf(x, dpp<kDppRowRor8>(x));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if (N >= 2) x += dpp<kDppXor1>(x);
+  if (N >= 4) x += dpp<kDppXor2>(x);
+  if (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if (N >= 16) x += dpp<kDppRowRor8>(x);
+  return x;
+}
+
 template <int HB>
 __global__ void __launch_bounds__(kAttnThreads)
 attn_kernel(AttnArgs a) {
@@ -59,7 +78,6 @@ attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float s_alpha[H];
   __shared__ float s_m[H], s_l[H];
   __shared__ int s_valid[kTileKeys];
-  __shared__ int s_rescale;
 
   const int r = blockIdx.x / a.n_split;
   const int sp = blockIdx.x - r * a.n_split;
@@ -71,18 +89,16 @@ attn_kernel(AttnArgs a) {
   const int G = lane >> 4;
   const int c = lane & 15;
 
+  // the per-row scalars are read together (none waits on another)
   int seq = a.row_seq[r];
+  int n_g = a.topk ? a.n_topk[r] : 0;
+  int64_t end = a.swa_kv ? a.swa_end[r] : 0;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   if (!seq_ok) seq = 0;
-  int n_g = 0;
-  if (a.topk && seq_ok) {
-    n_g = a.n_topk[r];
-    n_g = n_g < 0 ? 0 : (n_g > a.k_pos ? a.k_pos : n_g);
-  }
+  n_g = (!seq_ok || n_g < 0) ? 0 : (n_g > a.k_pos ? a.k_pos : n_g);
   int64_t s0 = 0;
   int n_s = 0;
   if (a.swa_kv && seq_ok) {
-    int64_t end = a.swa_end[r];
     end = end < 0 ? 0 : (end > a.swa_len ? a.swa_len : end);
     s0 = end - a.swa_window;
     s0 = s0 < 0 ? 0 : s0;
@@ -126,17 +142,16 @@ attn_kernel(AttnArgs a) {
         }
       }
   }
-  if (tid < H) {
-    float m0 = -INFINITY, l0 = 0.f;
-    if (merge_in) {
-      const float lin = a.lse[(int64_t)r * H + tid];
-      if (lin != -INFINITY) {
-        m0 = lin * 1.4426950408889634f;
-        l0 = 1.f;
-      }
+  // Softmax state of head tid / TPH, held by its TPH threads (consecutive
+  // lanes of one wave): the running max (log2 units) in every one of them,
+  // the normaliser as per-thread partial sums, reduced once at the end.
+  float m_run = -INFINITY, l_thr = 0.f;
+  if (merge_in) {
+    const float lin = a.lse[(int64_t)r * H + tid / TPH];
+    if (lin != -INFINITY) {
+      m_run = lin * 1.4426950408889634f;
+      l_thr = (tid % TPH) == 0 ? 1.f : 0.f;
     }
-    s_m[tid] = m0;
-    s_l[tid] = l0;
   }
 
   const uint8_t *kv_codes = a.kv_codes + (int64_t)seq * a.cap * 256;
@@ -144,14 +159,24 @@ attn_kernel(AttnArgs a) {
   const uint8_t *swa = a.swa_kv ? a.swa_kv + ((int64_t)seq * a.swa_len) * 512 : nullptr;
   const int32_t *topk = a.topk ? a.topk + (int64_t)r * a.k_pos : nullptr;
 
-  auto load_tile = [&](int tile) {
+  // Entry ids of a tile's two 16-key blocks (lane c: slots 16kb + c).  They
+  // are read ahead of need and without waiting for n_topk (every slot below
+  // k_pos is inside the row), so only the gather of the codes waits on an
+  // earlier load.
+  auto load_ids = [&](int tile, int32_t (&e)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int slot = tile * kTileKeys + 16 * kb + c;
+      e[kb] = (topk && slot < a.k_pos) ? topk[slot] : -1;
+    }
+  };
+  auto load_tile = [&](int tile, const int32_t (&ids)[2]) {
     RawTile t;
     if (tile < n_gt) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int slot = tile * kTileKeys + 16 * kb + c;
-        int64_t e = -1;
-        if (slot < n_g) e = topk[slot];
+        const int64_t e = slot < n_g ? ids[kb] : -1;
         const bool ok = e >= 0 && e < a.cap;
         t.valid[kb] = ok;
         const int64_t el = ok ? e : 0;
@@ -175,12 +200,19 @@ attn_kernel(AttnArgs a) {
     return t;
   };
 
+  // the first two tiles' ids are read before n_topk arrives (t_begin does
+  // not depend on it); slots past the row's count are masked in load_tile
+  int32_t ids_cur[2], ids_nxt[2];
+  load_ids(t_begin, ids_cur);
+  load_ids(t_begin + 1, ids_nxt);
   RawTile cur;
-  if (t_begin < t_end) cur = load_tile(t_begin);
+  if (t_begin < t_end) cur = load_tile(t_begin, ids_cur);
 
   for (int tile = t_begin; tile < t_end; ++tile) {
     RawTile nxt;
-    if (tile + 1 < t_end) nxt = load_tile(tile + 1);
+    if (tile + 1 < t_end) nxt = load_tile(tile + 1, ids_nxt);
+    int32_t ids_n2[2] = {-1, -1};
+    if (tile + 2 < t_end) load_ids(tile + 2, ids_n2);
     const bool is_swa = tile >= n_gt;
 
     // dequantise this wave's quarter of the 32 keys
@@ -213,7 +245,6 @@ attn_kernel(AttnArgs a) {
       s_valid[c] = cur.valid[0];
       s_valid[16 + c] = cur.valid[1];
     }
-    if (tid == 0) s_rescale = 0;
 
     // partial logits over this wave's channel quarter
 #pragma unroll
@@ -250,12 +281,10 @@ attn_kernel(AttnArgs a) {
         sv[j] = s;
         tmax = fmaxf(tmax, s);
       }
-#pragma unroll
-      for (int off = TPH / 2; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
-      const float m_old = s_m[h];
-      const float l_old = s_l[h];
-      float m_new = m_old;
-      if (m_old == -INFINITY || tmax > m_old + kLazyRescale) m_new = fmaxf(tmax, m_old);
+      tmax = group_max<TPH>(tmax);
+      float m_new = m_run;
+      if (m_run == -INFINITY || tmax > m_run + kLazyRescale) m_new = fmaxf(tmax, m_run);
+      const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
@@ -264,23 +293,19 @@ attn_kernel(AttnArgs a) {
         s_p[h * kPStride + kk0 + j] = ph;
         psum += (float)ph;
       }
-#pragma unroll
-      for (int off = TPH / 2; off > 0; off >>= 1) psum += __shfl_xor(psum, off);
-      const float alpha = (m_old == -INFINITY || m_new == m_old) ? 1.f : exp2f(m_old - m_new);
-      if ((tid % TPH) == 0) {
-        s_m[h] = m_new;
-        s_l[h] = l_old * alpha + psum;
-        s_alpha[h] = alpha;
-        if (alpha != 1.f) s_rescale = 1;
-      }
+      l_thr = l_thr * alpha + psum;
+      m_run = m_new;
+      if ((tid % TPH) == 0) s_alpha[h] = alpha;
     }
     __syncthreads();
 
-    // O[:, quarter] = alpha * O + P V
-    if (s_rescale) {
+    // O[:, quarter] = alpha * O + P V (the rescale is skipped while the
+    // running maxima of this wave's heads stand still)
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const float4 al = *reinterpret_cast<const float4 *>(&s_alpha[16 * hb + 4 * G]);
+    for (int hb = 0; hb < HB; ++hb) {
+      const float4 al = *reinterpret_cast<const float4 *>(&s_alpha[16 * hb + 4 * G]);
+      const bool move = al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f;
+      if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
           acc_o[hb][db][0] *= al.x;
@@ -312,8 +337,17 @@ attn_kernel(AttnArgs a) {
     }
     __syncthreads();
     cur = nxt;
+    ids_nxt[0] = ids_n2[0];
+    ids_nxt[1] = ids_n2[1];
   }
 
+  {
+    const float l = group_sum<TPH>(l_thr);
+    if ((tid % TPH) == 0) {
+      s_m[tid / TPH] = m_run;
+      s_l[tid / TPH] = l;
+    }
+  }
   __syncthreads();
   if (split) {
     // unnormalised partial: O, running max (log2 units) and sum per head

@@ -156,8 +156,20 @@ constexpr int kSelWaves = kSelThreads / 64;
 // lane-contiguous.
 constexpr int kKeysPerThread = kSelectChunk / kSelThreads;
 constexpr int kSelSpan = 64 * kKeysPerThread;
-// Keys left after the first radix digit that one wave finishes alone.
-constexpr int kCandCap = 4096;
+// Radix digits: up to 12 bits while the whole work-group counts, 10 bits once
+// one wave finishes alone on at most kCandCap keys gathered in LDS.
+constexpr int kSelBits = 12;
+constexpr int kSelBins = 1 << kSelBits;
+constexpr int kWaveBits = 10;
+constexpr int kCandCap = 2048;
+// First digit of the common case: a window of kSelBins bins of 2^kWinShift
+// key units ending at the largest key (for scores >= 0: the top four octaves
+// at 1/1024-octave resolution).  It is used when the keys span more than the
+// plain 12-bit first digit would resolve that finely.
+constexpr int kWinShift = 13;
+// (key, id) pairs at or above the threshold's window bin, kept in LDS in
+// position order.
+constexpr int kListCap = 4096;
 
 // Reductions over the 64 lanes of a wave (DPP inside 16-lane rows, then the
 // row swaps); every lane receives the result.
@@ -173,13 +185,19 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x, int lane, Op op) {
   return op(x, (uint32_t)(lane < 32 ? s32[1] : s32[0]));
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  return v;
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row
+// of 16 lanes (DPP, zero fill), then the totals of the lower rows added from
+// lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(x, 15);
+  const int t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row == 0 ? 0 : (row == 1 ? t0 : (row == 2 ? t0 + t1 : t0 + t1 + t2)));
 }
 
 // Orders the LDS accesses of one wave before and after it (no work-group
@@ -190,46 +208,59 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One wave finds the bin of a 256-bin histogram that holds the k_rem-th
-// largest key (bins scanned from the top); returns the bin and, through
-// *above, the number of keys in higher bins.
-__device__ __forceinline__ int find_digit(const uint32_t *hist, int k_rem, int lane, int *above) {
-  int cnt[4];
+struct Digit {
+  int digit;   // bin holding the k_rem-th largest key
+  int above;   // keys in higher bins
+  int count;   // keys in that bin
+  int total;   // keys in the whole histogram
+};
+
+// One wave finds, in a histogram of nb bins (a power of two, 2 .. 4096), the
+// bin that holds the k_rem-th largest key, counting from the top bin down.
+// Lane l first sums the l-th group of nb/64 bins from the top; a prefix sum
+// over the lanes names the group, and a second one over that group's bins
+// (one per lane) names the bin.
+__device__ __forceinline__ Digit find_digit(const uint32_t *hist, int nb, int k_rem, int lane) {
+  const int per = nb >= 64 ? nb / 64 : 1;
+  const int top = nb - lane * per;        // this lane's group: bins [top - per, top)
   int local = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    cnt[j] = (int)hist[255 - 4 * lane - j];
-    local += cnt[j];
-  }
-  const int incl = wave_incl_scan(local, lane);
-  const int excl = incl - local;
-  int digit = -1, abv = 0;
-  if (excl < k_rem && k_rem <= incl) {
-    int cum = excl;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (digit < 0 && cum + cnt[j] >= k_rem) {
-        digit = 255 - 4 * lane - j;
-        abv = cum;
+  if (top > 0) {
+    if (per >= 4) {
+      for (int i = 0; i < per; i += 4) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(&hist[top - per + i]);
+        local += (int)(v.x + v.y + v.z + v.w);
       }
-      cum += cnt[j];
+    } else {
+      for (int i = 0; i < per; ++i) local += (int)hist[top - per + i];
     }
   }
-  const unsigned long long owner = __ballot(digit >= 0);
-  const int src = __ffsll((long long)owner) - 1;
-  *above = __shfl(abv, src);
-  return __shfl(digit, src);
+  const int incl = wave_incl_scan(local, lane);
+  const unsigned long long hit = __ballot(incl >= k_rem);
+  const int o = hit ? __ffsll((long long)hit) - 1 : 0;      // the group holding the bin
+  const int excl_o = __builtin_amdgcn_readlane(incl - local, o);
+  const int gtop = nb - o * per;
+  const int c = lane < per ? (int)hist[gtop - 1 - lane] : 0;
+  const int cum = excl_o + wave_incl_scan(c, lane);
+  const unsigned long long hit2 = __ballot(lane < per && cum >= k_rem);
+  const int l2 = hit2 ? __ffsll((long long)hit2) - 1 : 0;
+  Digit d;
+  d.total = __builtin_amdgcn_readlane(incl, 63);
+  d.digit = gtop - 1 - l2;
+  d.count = __builtin_amdgcn_readlane(c, l2);
+  d.above = __builtin_amdgcn_readlane(cum, l2) - d.count;
+  return d;
 }
 
 template <bool FINAL, bool IDS>
 __global__ void __launch_bounds__(kSelThreads)
 select_kernel(SelectArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_cand[kCandCap];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kSelBins];
+  __shared__ uint32_t s_lkey[kListCap];   // the list's keys; the candidates of the generic path
+  __shared__ int32_t s_lid[kListCap];
   __shared__ int32_t s_pool[FINAL ? kMaxPoolBlocks : 1];
   __shared__ int s_red[kSelWaves * 2];
   __shared__ uint32_t s_min[kSelWaves], s_max[kSelWaves];
-  __shared__ int s_digit, s_above, s_ncand;
+  __shared__ int s_digit, s_above, s_ncand, s_flag;
   __shared__ uint32_t s_thr;
   __shared__ int s_keq;
 
@@ -294,8 +325,8 @@ select_kernel(SelectArgs a) {
     s_min[wave] = kmin;
     s_max[wave] = kmax;
   }
-  if (tid < 256) hist[tid] = 0;
-  if (tid == 0) s_ncand = 0;
+#pragma unroll
+  for (int i = 0; i < kSelBins / kSelThreads; ++i) hist[tid + kSelThreads * i] = 0;
   __syncthreads();
   int nv_all = 0;
   kmin = 0xFFFFFFFFu;
@@ -308,157 +339,283 @@ select_kernel(SelectArgs a) {
   }
   const int k_eff = nv_all < a.k ? nv_all : a.k;
 
-  // Radix select of the k_eff-th largest key.  Bits above the highest bit in
-  // which the smallest and largest valid keys differ are common to all valid
-  // keys, so the 8-bit digits start there.  After the first digit the keys
-  // still in play are usually few: one wave gathers them and finishes alone.
-  uint32_t thr = 0u;
-  int k_eq = 0;
-  if (k_eff < nv_all) {
-    const uint32_t diff = kmin ^ kmax;
-    if (diff == 0u) {
-      thr = kmin;
-      k_eq = k_eff;
-    } else {
-      const int hb = 31 - __clz(diff);
-      uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
-      uint32_t prefix = kmin & mask;
-      int k_rem = k_eff;
-      int top = hb;
-      bool wave_path = false;
-      while (top >= 0 && !wave_path) {
-        const int shift = top >= 7 ? top - 7 : 0;
-        const uint32_t dmask = (2u << (top - shift)) - 1u;
-#pragma unroll
-        for (int j = 0; j < kKeysPerThread; ++j)
-          if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
-        __syncthreads();
-        if (wave == 0) {
-          int above;
-          const int d = find_digit(hist, k_rem, lane, &above);
-          if (lane == 0) {
-            s_digit = d;
-            s_above = above;
-            s_ncand = (int)hist[d];
-          }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)s_digit << shift;
-        mask |= dmask << shift;
-        k_rem -= s_above;
-        const int ncand = s_ncand;
-        top = shift - 1;
-        __syncthreads();
-        if (tid < 256) hist[tid] = 0;
-        if (top >= 0 && ncand <= kCandCap) {
-          // gather the keys still in play
-          if (tid == 0) s_ncand = 0;
-          __syncthreads();
-          const unsigned long long lt = (1ull << lane) - 1ull;
-#pragma unroll
-          for (int j = 0; j < kKeysPerThread; ++j) {
-            const bool m = key[j] != 0u && (key[j] & mask) == prefix;
-            const unsigned long long bm = __ballot(m);
-            if (bm) {
-              int off = 0;
-              if (lane == 0) off = atomicAdd(&s_ncand, __popcll(bm));
-              off = __shfl(off, 0);
-              if (m) s_cand[off + __popcll(bm & lt)] = key[j];
-            }
-          }
-          wave_path = true;
-        }
-        __syncthreads();
-      }
-      if (wave_path) {
-        if (wave == 0) {
-          const int ncand = s_ncand;
-          while (top >= 0) {
-            const int shift = top >= 7 ? top - 7 : 0;
-            const uint32_t dmask = (2u << (top - shift)) - 1u;
-            for (int i = lane; i < ncand; i += 64) {
-              const uint32_t k = s_cand[i];
-              if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-            }
-            wave_sync();
-            int above;
-            const int d = find_digit(hist, k_rem, lane, &above);
-            prefix |= (uint32_t)d << shift;
-            mask |= dmask << shift;
-            k_rem -= above;
-            wave_sync();
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
-            wave_sync();
-            top = shift - 1;
-          }
-          if (lane == 0) {
-            s_thr = prefix;
-            s_keq = k_rem;
-          }
-        }
-        __syncthreads();
-        thr = s_thr;
-        k_eq = s_keq;
-      } else {
-        thr = prefix;
-        k_eq = k_rem;
-      }
-    }
-  }
-
-  // Ordered compaction from registers: a key's output position is (#keys
-  // above the threshold before it) + min(#threshold ties before it, k_eq),
-  // counted with ballots; ties are taken lowest position first.
-  uint32_t cgt = 0, ceq = 0;
-#pragma unroll
-  for (int j = 0; j < kKeysPerThread; ++j) {
-    cgt += key[j] > thr;
-    ceq += (key[j] == thr) && (base + 64 * j < n);
-  }
-  cgt = wave_reduce(cgt, lane, [](uint32_t x, uint32_t y) { return x + y; });
-  ceq = wave_reduce(ceq, lane, [](uint32_t x, uint32_t y) { return x + y; });
-  if (lane == 0) {
-    s_red[wave] = (int)cgt;
-    s_red[kSelWaves + wave] = (int)ceq;
-  }
-  __syncthreads();
-  int run_gt = 0, run_eq = 0;
-  for (int v = 0; v < wave; ++v) {
-    run_gt += s_red[v];
-    run_eq += s_red[kSelWaves + v];
-  }
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
   int32_t *out = FINAL ? a.out + (int64_t)r * a.k : nullptr;
   uint32_t *kout = FINAL ? nullptr : a.keys_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
   int32_t *iout = FINAL ? nullptr : a.ids_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
+  // writes kept key k (carried id or chunk position `id`) to output slot pos
+  auto emit = [&](int pos, uint32_t k, int id) {
+    if (FINAL) {
+      if (a.map_kind == kMapPool) {
+        const int p = id >> 3;
+        const int b = (p < np) ? s_pool[p] : -1;
+        id = b * 8 + (id & 7);
+      }
+      out[pos] = id;
+    } else {
+      kout[pos] = k;
+      iout[pos] = id;
+    }
+  };
+
+  // Common case: the window pass.  Its histogram names the window bin that
+  // holds the k_eff-th largest key; every key at or above that bin goes, in
+  // position order, into an LDS list (about k_eff keys plus one bin), one wave
+  // resolves the remaining 13 bits on the list, and the output is compacted
+  // from the list.  Used when the keys spread beyond a plain 12-bit digit's
+  // resolution; falls back to the generic path when the k_eff-th key lies
+  // below the window or the list would overflow.
+  bool listed = false;
+  if (k_eff < nv_all && kmin != kmax && 31 - __clz(kmin ^ kmax) > kWinShift + kSelBits - 1) {
+    const uint32_t top_bin = kmax >> kWinShift;
+    const uint32_t base_bin = top_bin >= (uint32_t)(kSelBins - 1) ? top_bin - (kSelBins - 1) : 0u;
 #pragma unroll
-  for (int j = 0; j < kKeysPerThread; ++j) {
-    const int i = base + 64 * j;
-    const uint32_t k = key[j];
-    const bool gt = k > thr;
-    const bool eq = (k == thr) && i < n;
-    const unsigned long long bgt = __ballot(gt), beq = __ballot(eq);
-    const int my_gt = run_gt + __popcll(bgt & lt_mask);
-    const int my_eq = run_eq + __popcll(beq & lt_mask);
-    run_gt += __popcll(bgt);
-    run_eq += __popcll(beq);
-    if (gt || (eq && my_eq < k_eq)) {
-      const int pos = my_gt + (my_eq < k_eq ? my_eq : k_eq);
-      int id = IDS ? ids[j] : (int)(start + i);
-      if (FINAL) {
-        if (a.map_kind == kMapPool) {
-          const int p = id >> 3;
-          const int b = (p < np) ? s_pool[p] : -1;
-          id = b * 8 + (id & 7);
-        }
-        out[pos] = id;
-      } else {
-        kout[pos] = k;
-        iout[pos] = id;
+    for (int j = 0; j < kKeysPerThread; ++j)
+      if (key[j] != 0u && (key[j] >> kWinShift) >= base_bin) atomicAdd(&hist[(key[j] >> kWinShift) - base_bin], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      const Digit d = find_digit(hist, kSelBins, k_eff, lane);
+      if (lane == 0) {
+        s_digit = d.digit;
+        s_above = d.above;
+        s_ncand = d.count;
+        s_flag = d.total >= k_eff && d.above + d.count <= kListCap;
       }
     }
+    __syncthreads();
+    listed = s_flag != 0;
+    if (listed) {
+      // bins 0 .. 191 serve the two refining passes below
+      if (tid < 192) hist[tid] = 0;
+      const uint32_t lo_key = (base_bin + (uint32_t)s_digit) << kWinShift;
+      const int n_list = s_above + s_ncand;
+      const unsigned long long lt = (1ull << lane) - 1ull;
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kKeysPerThread; ++j) cnt += __popcll(__ballot(key[j] != 0u && key[j] >= lo_key));
+      if (lane == 0) s_red[wave] = cnt;
+      __syncthreads();
+      int off = 0;
+      for (int v = 0; v < wave; ++v) off += s_red[v];
+#pragma unroll
+      for (int j = 0; j < kKeysPerThread; ++j) {
+        const bool m = key[j] != 0u && key[j] >= lo_key;
+        const unsigned long long bm = __ballot(m);
+        if (m) {
+          const int e = off + __popcll(bm & lt);
+          s_lkey[e] = key[j];
+          s_lid[e] = IDS ? ids[j] : (int)(start + base + 64 * j);
+        }
+        off += __popcll(bm);
+      }
+      __syncthreads();
+      // The remaining 13 bits, from the list held in registers (thread t:
+      // entries 4t .. 4t+3): bits 12..6 counted in bins 0..127, bits 5..0 in
+      // bins 128..191.
+      uint32_t lk[4];
+      int32_t li[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        lk[q] = e < n_list ? s_lkey[e] : 0u;
+        li[q] = e < n_list ? s_lid[e] : -1;
+      }
+      uint32_t prefix = lo_key;
+      int k_rem = k_eff - s_above;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lk[q] != 0u && (lk[q] >> kWinShift) == (prefix >> kWinShift)) atomicAdd(&hist[(lk[q] >> 6) & 127u], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        const Digit d = find_digit(hist, 128, k_rem, lane);
+        if (lane == 0) {
+          s_digit = d.digit;
+          s_above = d.above;
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << 6;
+      k_rem -= s_above;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lk[q] != 0u && (lk[q] >> 6) == (prefix >> 6)) atomicAdd(&hist[128 + (lk[q] & 63u)], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        const Digit d = find_digit(hist + 128, 64, k_rem, lane);
+        if (lane == 0) {
+          s_thr = prefix | (uint32_t)d.digit;
+          s_keq = k_rem - d.above;
+        }
+      }
+      __syncthreads();
+      const uint32_t thr = s_thr;
+      const int k_eq = s_keq;
+      // ordered compaction of the list; above-threshold and tie counts
+      // travel packed in one prefix sum
+      int packed = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) packed += (int)(lk[q] > thr) + ((int)(lk[q] == thr) << 16);
+      const int incl = wave_incl_scan(packed, lane);
+      if (lane == 63) s_red[wave] = incl;
+      __syncthreads();
+      int run = incl - packed;
+      for (int v = 0; v < wave; ++v) run += s_red[v];
+      int run_gt = run & 0xFFFF, run_eq = run >> 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool gt = lk[q] > thr;
+        const bool eq = lk[q] == thr;
+        if (gt || (eq && run_eq < k_eq)) emit(run_gt + (run_eq < k_eq ? run_eq : k_eq), lk[q], li[q]);
+        run_gt += gt;
+        run_eq += eq;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSelBins / kSelThreads; ++i) hist[tid + kSelThreads * i] = 0;
+      __syncthreads();
+    }
   }
+
+  // Generic path.  Radix select of the k_eff-th largest key.  Bits above the highest bit in
+  // which the smallest and largest valid keys differ are common to all valid
+  // keys, so the digits start there: 12-bit digits counted by the whole
+  // work-group from registers, until the keys still in play fit in LDS; one
+  // wave then gathers nothing more and finishes them with 10-bit digits.
+  if (!listed) {
+    uint32_t thr = 0u;
+    int k_eq = 0;
+    if (k_eff < nv_all) {
+      const uint32_t diff = kmin ^ kmax;
+      if (diff == 0u) {
+        thr = kmin;
+        k_eq = k_eff;
+      } else {
+        const int hb = 31 - __clz(diff);
+        uint32_t mask = hb >= 31 ? 0u : ~((2u << hb) - 1u);
+        uint32_t prefix = kmin & mask;
+        int k_rem = k_eff;
+        int top = hb;
+        bool gathered = false;
+        while (top >= 0) {
+          const int width = top + 1 < kSelBits ? top + 1 : kSelBits;
+          const int shift = top + 1 - width;
+          const uint32_t dmask = (1u << width) - 1u;
+  #pragma unroll
+          for (int j = 0; j < kKeysPerThread; ++j)
+            if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+          __syncthreads();
+          if (wave == 0) {
+            const Digit d = find_digit(hist, 1 << width, k_rem, lane);
+            if (lane == 0) {
+              s_digit = d.digit;
+              s_above = d.above;
+              s_ncand = d.count;
+            }
+          }
+          __syncthreads();
+          prefix |= (uint32_t)s_digit << shift;
+          mask |= dmask << shift;
+          k_rem -= s_above;
+          const int ncand = s_ncand;
+          top = shift - 1;
+  #pragma unroll
+          for (int i = 0; i < kSelBins / kSelThreads; ++i) hist[tid + kSelThreads * i] = 0;
+          if (top >= 0 && ncand <= kCandCap) {
+            // gather the keys still in play, wave by wave (per-wave counts,
+            // then each wave's offset)
+            const unsigned long long lt = (1ull << lane) - 1ull;
+            int cnt = 0;
+  #pragma unroll
+            for (int j = 0; j < kKeysPerThread; ++j)
+              cnt += __popcll(__ballot(key[j] != 0u && (key[j] & mask) == prefix));
+            if (lane == 0) s_red[wave] = cnt;
+            __syncthreads();
+            int off = 0;
+            for (int v = 0; v < wave; ++v) off += s_red[v];
+  #pragma unroll
+            for (int j = 0; j < kKeysPerThread; ++j) {
+              const bool m = key[j] != 0u && (key[j] & mask) == prefix;
+              const unsigned long long bm = __ballot(m);
+              if (m) s_lkey[off + __popcll(bm & lt)] = key[j];
+              off += __popcll(bm);
+            }
+            gathered = true;
+          }
+          __syncthreads();
+          if (gathered) break;
+        }
+        if (gathered) {
+          if (wave == 0) {
+            const int ncand = s_ncand;
+            while (top >= 0) {
+              const int width = top + 1 < kWaveBits ? top + 1 : kWaveBits;
+              const int shift = top + 1 - width;
+              const uint32_t dmask = (1u << width) - 1u;
+              for (int i = lane; i < ncand; i += 64) {
+                const uint32_t k = s_lkey[i];
+                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+              }
+              wave_sync();
+              const Digit d = find_digit(hist, 1 << width, k_rem, lane);
+              prefix |= (uint32_t)d.digit << shift;
+              mask |= dmask << shift;
+              k_rem -= d.above;
+              wave_sync();
+              for (int i = lane; i < (1 << width); i += 64) hist[i] = 0;
+              wave_sync();
+              top = shift - 1;
+            }
+            if (lane == 0) {
+              s_thr = prefix;
+              s_keq = k_rem;
+            }
+          }
+          __syncthreads();
+          thr = s_thr;
+          k_eq = s_keq;
+        } else {
+          thr = prefix;
+          k_eq = k_rem;
+        }
+      }
+    }
+
+    // Ordered compaction from registers: a key's output position is (#keys
+    // above the threshold before it) + min(#threshold ties before it, k_eq),
+    // counted with ballots; ties are taken lowest position first.
+    uint32_t cgt = 0, ceq = 0;
+  #pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+      cgt += key[j] > thr;
+      ceq += (key[j] == thr) && (base + 64 * j < n);
+    }
+    cgt = wave_reduce(cgt, lane, [](uint32_t x, uint32_t y) { return x + y; });
+    ceq = wave_reduce(ceq, lane, [](uint32_t x, uint32_t y) { return x + y; });
+    if (lane == 0) {
+      s_red[wave] = (int)cgt;
+      s_red[kSelWaves + wave] = (int)ceq;
+    }
+    __syncthreads();
+    int run_gt = 0, run_eq = 0;
+    for (int v = 0; v < wave; ++v) {
+      run_gt += s_red[v];
+      run_eq += s_red[kSelWaves + v];
+    }
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  #pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+      const int i = base + 64 * j;
+      const uint32_t k = key[j];
+      const bool gt = k > thr;
+      const bool eq = (k == thr) && i < n;
+      const unsigned long long bgt = __ballot(gt), beq = __ballot(eq);
+      const int my_gt = run_gt + __popcll(bgt & lt_mask);
+      const int my_eq = run_eq + __popcll(beq & lt_mask);
+      run_gt += __popcll(bgt);
+      run_eq += __popcll(beq);
+      if (gt || (eq && my_eq < k_eq))
+        emit(my_gt + (my_eq < k_eq ? my_eq : k_eq), k, IDS ? ids[j] : (int)(start + i));
+    }
+  }  // generic path
   if (FINAL) {
     for (int i = k_eff + tid; i < a.k; i += kSelThreads) out[i] = -1;
     if (tid == 0) a.n_out[r] = k_eff;
