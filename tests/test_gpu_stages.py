@@ -174,6 +174,38 @@ def test_index_full_flat_mode(csa2, n_vis_rows):
         check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], "flat")
 
 
+@pytest.mark.parametrize("kind", ["outlier", "tied_block", "narrow_spread"])
+def test_index_flat_selection_regimes(csa2, kind):
+    """Score distributions that steer the selection off its common case:
+    a few outliers far above the rest (the k-th score lies far below the
+    maximum), thousands of identical top scores (a tie block larger than any
+    candidate list), and scores that all lie within one octave."""
+    n, k_pos = 20000, 512
+    base = W.rms_rows(n, 128, seed=71).numpy()
+    qidx = W.bf16_normal((2, 8, 128), seed=72)
+    w = W.uniform01((2, 8), seed=73)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    ikc0, iks0 = oracle.quantize(base, 32)
+    s0 = oracle.index_scores(qb[0], wn[0], ikc0, iks0, np.arange(n))
+    ik = base.copy()
+    if kind == "outlier":
+        ik[:10] *= 200.0
+    elif kind == "tied_block":
+        ik[3000:9000] = 2.0 * base[int(np.argmax(s0))]
+    else:
+        med = np.median(s0[s0 > 0])
+        band = np.flatnonzero((s0 > med) & (s0 < 1.6 * med))
+        ik = base[band[np.arange(n) % len(band)]]
+    lat = W.rms_rows(n, 512, seed=74).numpy()
+    cache, ora = build_cache(csa2, [lat], [ik], n)
+    _, _, ikc, iks = ora[0]
+    _, _, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [0, 0], [n, n - 7], n, 0, k_pos)
+    for r, nv in enumerate([n, n - 7]):
+        ref = oracle.full_layer_select(qb[r], wn[r], ikc, iks, nv, 0, k_pos)
+        sc = ref["entry_scores"]
+        check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], kind)
+
+
 def test_index_reindex_on_oracle_pool(csa2):
     n_list = [9000, 3001]
     cache, ora = make_index_case(csa2, n_list, 9000, seed=23)
