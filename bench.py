@@ -25,6 +25,7 @@ timed with HIP events recorded between the graph launches on the stream
 they run on; cpu_baseline = the oracle on a bounded sample of the same step.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -37,6 +38,33 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 IK_BYTES = 68                  # indexer key bytes per entry (64 codes + 4 scales)
+BLOCK_KEY_BYTES = 4            # the scan writes one 4-B key per block of 8 entries
+
+# HBM bytes per scan launch from two rocprofv3 counter runs of this bench
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same
+# counter reads for a plain 512-MiB device copy.  They describe the scan kernel
+# as built from these sources; once the sources differ the figure is dropped.
+SCAN_COUNTERS = {
+    "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
+                "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
+                "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
+    "sha256": "38fc0fb280ef78d261a1a8ed9f799b3007cb130b9c9027e9573265f99ee2fdb0",
+    "fetch_kib": 278651.198, "fetch_scale": 524288 / 262166.875,
+    "write_kib": 4325.568, "write_scale": 524288 / 524288.0,
+}
+
+
+def scan_traffic_bytes():
+    """Counter-measured HBM bytes per scan launch, or None when the scan's
+    sources changed since the counters were taken."""
+    h = hashlib.sha256()
+    for f in SCAN_COUNTERS["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != SCAN_COUNTERS["sha256"]:
+        return None
+    c = SCAN_COUNTERS
+    return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
 SCALE = 1.0 / math.sqrt(512)
 
 
@@ -49,6 +77,9 @@ def parse():
                     help="query rows of the step the oracle runs for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ctx", type=int, default=None, help="override the context (testing only)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the steps, copy a MIB-MiB buffer once with a plain device copy "
+                         "(a known-size kernel for scaling hardware byte counters)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as HIP graphs instead of launching every kernel from Python")
     return ap.parse_args()
@@ -340,6 +371,14 @@ def main():
     torch.cuda.set_device(0)
     import fp4_compressed_sparse_e2m1_amd as csa2
     csa2.load()
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_build = time.perf_counter()
     c = build(args.ctx)
     t_build = time.perf_counter() - t_build
@@ -347,7 +386,9 @@ def main():
     B, T, L = c["B"], c["T"], c["L"]
     ms_step = wall * 1e3 / args.steps
     value = B * L / (wall / args.steps)
-    scan_bytes = IK_BYTES * T * B
+    # algorithmic bytes of one scan launch: every entry's indexer key read
+    # once, one block key written per 8 entries
+    scan_bytes = IK_BYTES * T * B + BLOCK_KEY_BYTES * ((T + 7) // 8) * B
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     modes = c["wl"].layers
     mode_us = {m: 1e3 * sum(t for t, mm in zip(per_layer, modes) if mm == m) /
@@ -372,7 +413,7 @@ def main():
                    "launch": "HIP graph replay (append, scan, rest)" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "kernel": "score_kernel<block max> (csa2_index_scan)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic_bytes(),
                      "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(scan_ms * 1e3, 2)},
         "per_layer_us_eager": {k: round(v, 2) for k, v in mode_us.items()},
         "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
