@@ -205,14 +205,11 @@ attn_kernel(AttnArgs a) {
   int32_t ids_cur[2], ids_nxt[2];
   load_ids(t_begin, ids_cur);
   load_ids(t_begin + 1, ids_nxt);
-  RawTile cur;
-  if (t_begin < t_end) cur = load_tile(t_begin, ids_cur);
+  RawTile ta, tb;
+  if (t_begin < t_end) ta = load_tile(t_begin, ids_cur);
 
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    RawTile nxt;
-    if (tile + 1 < t_end) nxt = load_tile(tile + 1, ids_nxt);
-    int32_t ids_n2[2] = {-1, -1};
-    if (tile + 2 < t_end) load_ids(tile + 2, ids_n2);
+  // One tile: dequantise, partial logits, online softmax, P.V.
+  auto compute_tile = [&](const RawTile &cur, int tile) {
     const bool is_swa = tile >= n_gt;
 
     // dequantise this wave's quarter of the 32 keys
@@ -336,9 +333,22 @@ attn_kernel(AttnArgs a) {
       for (int db = 0; db < 8; ++db) acc_o[hb][db] = mfma16x16x32(pa, vb[db], acc_o[hb][db]);
     }
     __syncthreads();
-    cur = nxt;
-    ids_nxt[0] = ids_n2[0];
-    ids_nxt[1] = ids_n2[1];
+  };
+
+  // Two tiles per trip with alternating registers, so the prefetched tile is
+  // never copied into the current one.
+  for (int tile = t_begin; tile < t_end; tile += 2) {
+    if (tile + 1 < t_end) tb = load_tile(tile + 1, ids_nxt);
+    int32_t ids_n2[2] = {-1, -1};
+    if (tile + 2 < t_end) load_ids(tile + 2, ids_n2);
+    compute_tile(ta, tile);
+    if (tile + 1 >= t_end) break;
+    if (tile + 2 < t_end) ta = load_tile(tile + 2, ids_n2);
+    int32_t ids_n3[2] = {-1, -1};
+    if (tile + 3 < t_end) load_ids(tile + 3, ids_n3);
+    compute_tile(tb, tile + 1);
+    ids_nxt[0] = ids_n3[0];
+    ids_nxt[1] = ids_n3[1];
   }
 
   {
@@ -402,20 +412,31 @@ attn_merge_kernel(AttnArgs a, int H) {
   const int h0 = 2 * (blockIdx.x - r * per_row);
   const int tid = threadIdx.x;
   const int ns = a.n_split;
+  const int hh = tid >> 7;                 // which of the two heads
+  const int d = (tid & 127) * 4;           // four channels
+  const int h = h0 + hh;
+  const float *po = a.part_o + (((int64_t)r * ns) * H + h) * 512 + d;
+  // The first (up to) kMergeBatch splits' partials are requested before the
+  // weights are known, so their loads overlap the weight computation.
+  constexpr int kMergeBatch = 16;
+  float4 v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    if (u < ns) v[u] = *reinterpret_cast<const float4 *>(po + (int64_t)u * H * 512);
   // wave 0 weighs the splits of head h0, wave 1 those of head h0 + 1; lane s
   // holds split s
   const int lane = tid & 63;
   const int wv = tid >> 6;
   if (wv < 2) {
-    const int h = h0 + wv;
+    const int hw = h0 + wv;
     float m_in = -INFINITY;
     if (a.merge_in) {
-      const float lin = a.lse[(int64_t)r * H + h];
+      const float lin = a.lse[(int64_t)r * H + hw];
       if (lin != -INFINITY) m_in = lin * 1.4426950408889634f;
     }
     float m = -INFINITY, l = 0.f;
     if (lane < ns) {
-      const float *ml = a.part_ml + (((int64_t)r * ns + lane) * H + h) * 2;
+      const float *ml = a.part_ml + (((int64_t)r * ns + lane) * H + hw) * 2;
       m = ml[0];
       l = ml[1];
     }
@@ -437,33 +458,26 @@ attn_merge_kernel(AttnArgs a, int H) {
     }
   }
   __syncthreads();
-  const int hh = tid >> 7;                 // which of the two heads
-  const int d = (tid & 127) * 4;           // four channels
-  const int h = h0 + hh;
   const float L = s_L[hh];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float *po = a.part_o + (((int64_t)r * ns) * H + h) * 512 + d;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    float4 v[4];
+  // splits in ascending order (a fixed summation order)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4 *>(po + (int64_t)(s + u) * H * 512);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float wgt = s_w[hh][s + u];
+  for (int u = 0; u < kMergeBatch; ++u) {
+    if (u < ns) {
+      const float wgt = s_w[hh][u];
       acc.x += wgt * v[u].x;
       acc.y += wgt * v[u].y;
       acc.z += wgt * v[u].z;
       acc.w += wgt * v[u].w;
     }
   }
-  for (; s < ns; ++s) {
-    const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)s * H * 512);
+  for (int s = kMergeBatch; s < ns; ++s) {
+    const float4 x = *reinterpret_cast<const float4 *>(po + (int64_t)s * H * 512);
     const float wgt = s_w[hh][s];
-    acc.x += wgt * v.x;
-    acc.y += wgt * v.y;
-    acc.z += wgt * v.z;
-    acc.w += wgt * v.w;
+    acc.x += wgt * x.x;
+    acc.y += wgt * x.y;
+    acc.z += wgt * x.z;
+    acc.w += wgt * x.w;
   }
   float4 *orow = reinterpret_cast<float4 *>(a.o + ((int64_t)r * H + h) * 512 + d);
   const float win = s_w[hh][ns];
