@@ -94,6 +94,23 @@ __device__ __forceinline__ float max8(float m) {
   return fmax2(m, dpp<kDppHalfMirror>(m));
 }
 
+// Value of lane l ^ 16: the 16-lane rows of each half wave trade places
+// (ds_swizzle in bit-mask mode: and 0x1F, or 0, xor 0x10; no LDS memory).
+__device__ __forceinline__ float swap_rows16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// Maximum of unsigned keys over each aligned group of 8 lanes, in every lane
+// of the group.
+__device__ __forceinline__ uint32_t umax8(uint32_t k) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, false);
+  k = k > o ? k : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, false);
+  k = k > o ? k : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x141, 0xF, 0xF, false);
+  return k > o ? k : o;
+}
+
 // Value of lane l + 16 for lanes 0..15 (and 32..47): the odd 16-lane rows are
 // swapped into the even ones.
 __device__ __forceinline__ float from_next_row(float x) {

@@ -33,6 +33,8 @@
 #include "device.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace csa2 {
 namespace {
 
@@ -43,7 +45,7 @@ constexpr int kScoreThreads = 256;
 template <int MODE>
 constexpr int score_chunk() { return MODE == kScorePool ? kScorePoolChunk : kScoreChunk; }
 
-template <int MODE, int U = (MODE == kScorePool ? 4 : 2), int CHUNK = score_chunk<MODE>(),
+template <int MODE, int U = 4, int CHUNK = score_chunk<MODE>(),
           bool ILV = false, bool ROWFAST = false>
 __global__ void __launch_bounds__(kScoreThreads)
 score_kernel(ScoreArgs a) {
@@ -97,54 +99,79 @@ score_kernel(ScoreArgs a) {
   auto tile_slot0 = [&](int t) -> int64_t {
     return ILV ? chunk0 + ((int64_t)t * 4 + wave) * 16 : chunk0 + ((int64_t)wave * kTilesPerWave + t) * 16;
   };
-  for (int tb = 0; tb < kTilesPerWave; tb += U) {
-    if (tile_slot0(tb) >= n_slots) break;
-    uint4 craw[U];
-    uint32_t sraw[U];
-    int64_t slot[U];
-    bool valid[U];
+  // FULL: every slot of the chunk is a visible entry (all chunks of a scan
+  // but a row's last), so loads need no masking and the tiles' addresses are
+  // constant offsets from one base.
+  const bool block_writer = lane < 16 && (c & 7) == 0;
+  auto run = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    // FULL: this lane's code / scale addresses of tile 0; tile t adds a
+    // constant (the tiles of a chunk are at fixed distances)
+    const int64_t slot00 = tile_slot0(0) + c;
+    const uint8_t *cbase = codes_base + slot00 * 64 + 16 * G;
+    const uint8_t *sbase = scales_base + slot00 * 4 + G;
+    for (int tb = 0; tb < kTilesPerWave; tb += U) {
+      if (!FULL && tile_slot0(tb) >= n_slots) break;
+      uint4 craw[U];
+      uint32_t sraw[U];
+      int64_t slot[U];
+      bool valid[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      slot[u] = tile_slot0(tb + u) + c;
-      int64_t entry;
-      if (MODE == kScorePool) {
-        const int64_t p = slot[u] >> 3;
-        int b = -1;
-        if (p < np) b = a.pool_blocks[(int64_t)r * a.k_blocks + p];
-        entry = (int64_t)b * 8 + (slot[u] & 7);
-        valid[u] = (p < np) && b >= 0 && entry < n_vis;
-      } else {
-        entry = slot[u];
-        valid[u] = entry < n_vis;
+      for (int u = 0; u < U; ++u) {
+        slot[u] = tile_slot0(tb + u) + c;
+        if (FULL) {
+          const int64_t d = ILV ? ((int64_t)(tb + u) * 4) * 16 : (int64_t)(tb + u) * 16;
+          valid[u] = true;
+          craw[u] = *reinterpret_cast<const uint4 *>(cbase + d * 64);
+          sraw[u] = sbase[d * 4];
+          continue;
+        }
+        int64_t entry;
+        if (MODE == kScorePool) {
+          const int64_t p = slot[u] >> 3;
+          int b = -1;
+          if (p < np) b = a.pool_blocks[(int64_t)r * a.k_blocks + p];
+          entry = (int64_t)b * 8 + (slot[u] & 7);
+          valid[u] = (p < np) && b >= 0 && entry < n_vis;
+        } else {
+          entry = slot[u];
+          valid[u] = entry < n_vis;
+        }
+        const int64_t e_ld = valid[u] ? entry : 0;
+        craw[u] = *reinterpret_cast<const uint4 *>(codes_base + e_ld * 64 + 16 * G);
+        sraw[u] = scales_base[e_ld * 4 + G];
       }
-      const int64_t e_ld = valid[u] ? entry : 0;
-      craw[u] = *reinterpret_cast<const uint4 *>(codes_base + e_ld * 64 + 16 * G);
-      sraw[u] = scales_base[e_ld * 4 + G];
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const _Float16 s = e4m3_to_f16(sraw[u]);
-      const f16x8 sv = f16x8{s, s, s, s, s, s, s, s};
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16x16x32(qa[0], e2m1x8_to_f16(craw[u].x) * sv, acc);
-      acc = mfma16x16x32(qa[1], e2m1x8_to_f16(craw[u].y) * sv, acc);
-      acc = mfma16x16x32(qa[2], e2m1x8_to_f16(craw[u].z) * sv, acc);
-      acc = mfma16x16x32(qa[3], e2m1x8_to_f16(craw[u].w) * sv, acc);
-      // lane (G, c): d[head 4G + i][entry c]; heads 8..15 are zero padding
-      float part = wh[0] * relu(acc[0]) + wh[1] * relu(acc[1]);
-      part += wh[2] * relu(acc[2]) + wh[3] * relu(acc[3]);
-      const float score = part + from_next_row(part);     // heads 0..3 + heads 4..7
-      if (MODE == kScoreBlockMax) {
-        const float m = max8(valid[u] ? score : -INFINITY);
-        const int64_t blk = slot[u] >> 3;
-        if (lane < 16 && (c & 7) == 0 && blk * 8 < n_slots) out_row[blk] = score_key(m);
-      } else if (MODE == kScoreFlat) {
-        if (lane < 16 && valid[u]) out_row[slot[u]] = score_key(score);
-      } else {
-        if (lane < 16 && slot[u] < n_slots) out_row[slot[u]] = valid[u] ? score_key(score) : 0u;
+      for (int u = 0; u < U; ++u) {
+        const _Float16 s = e4m3_to_f16(sraw[u]);
+        const f16x8 sv = f16x8{s, s, s, s, s, s, s, s};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16x16x32(qa[0], e2m1x8_to_f16(craw[u].x) * sv, acc);
+        acc = mfma16x16x32(qa[1], e2m1x8_to_f16(craw[u].y) * sv, acc);
+        acc = mfma16x16x32(qa[2], e2m1x8_to_f16(craw[u].z) * sv, acc);
+        acc = mfma16x16x32(qa[3], e2m1x8_to_f16(craw[u].w) * sv, acc);
+        // lane (G, c): d[head 4G + i][entry c]; heads 8..15 are zero padding
+        float part = wh[0] * relu(acc[0]) + wh[1] * relu(acc[1]);
+        part += wh[2] * relu(acc[2]) + wh[3] * relu(acc[3]);
+        const float score = part + swap_rows16(part);   // heads 0..3 + heads 4..7
+        if (MODE == kScoreBlockMax) {
+          uint32_t key = score_key(score);
+          if (!FULL) key = valid[u] ? key : 0u;
+          key = umax8(key);
+          const int64_t blk = slot[u] >> 3;
+          if (block_writer && (FULL || blk * 8 < n_slots)) out_row[blk] = key;
+        } else if (MODE == kScoreFlat) {
+          if (lane < 16 && valid[u]) out_row[slot[u]] = score_key(score);
+        } else {
+          if (lane < 16 && slot[u] < n_slots) out_row[slot[u]] = valid[u] ? score_key(score) : 0u;
+        }
       }
     }
-  }
+  };
+  if (MODE != kScorePool && chunk0 + kChunk <= n_slots)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // ------------------------------------------------------------- selection
