@@ -128,9 +128,11 @@ score_kernel(ScoreArgs a) {
         }
         int64_t entry;
         if (MODE == kScorePool) {
+          // the pool id is read whether or not p < n_pool (every p below
+          // k_blocks is inside the pool row), so the read need not wait for
+          // the count
           const int64_t p = slot[u] >> 3;
-          int b = -1;
-          if (p < np) b = a.pool_blocks[(int64_t)r * a.k_blocks + p];
+          const int b = a.pool_blocks[(int64_t)r * a.k_blocks + p];
           entry = (int64_t)b * 8 + (slot[u] & 7);
           valid[u] = (p < np) && b >= 0 && entry < n_vis;
         } else {
@@ -311,14 +313,18 @@ select_kernel(SelectArgs a) {
   int n = (int)((int64_t)n_row - start);
   n = n < 0 ? 0 : (n > kSelectChunk ? kSelectChunk : n);
 
-  // keys (and carried ids) into registers
+  // keys (and carried ids) into registers.  The loads are bounded by the
+  // row's stride, which the host knows, not by the row's count n, so they do
+  // not wait for the count; positions at or past n are cleared afterwards.
   const uint32_t *kin = a.keys_in + (int64_t)r * a.in_stride + start;
+  const int64_t in_left = a.in_stride - start;
+  const int n_ld = in_left < kSelectChunk ? (int)in_left : kSelectChunk;
   const int base = wave * kSelSpan + lane;
   uint32_t key[kKeysPerThread];
 #pragma unroll
   for (int j = 0; j < kKeysPerThread; ++j) {
     const int i = base + 64 * j;
-    key[j] = i < n ? kin[i] : 0u;
+    key[j] = i < n_ld ? kin[i] : 0u;
   }
   int32_t ids[IDS ? kKeysPerThread : 1];
   if (IDS) {
@@ -326,15 +332,23 @@ select_kernel(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j) {
       const int i = base + 64 * j;
-      ids[j] = i < n ? idin[i] : -1;
+      ids[j] = i < n_ld ? idin[i] : -1;
     }
   }
-  // the pool row, for mapping candidate slots to entries
+  // the pool row, for mapping candidate slots to entries (read in full;
+  // slots past n_pool are masked when mapped)
   int np = 0;
   if (FINAL && a.map_kind == kMapPool) {
+    for (int i = tid; i < a.k_blocks; i += kSelThreads) s_pool[i] = a.pool_blocks[(int64_t)r * a.k_blocks + i];
     np = a.n_pool[r];
     np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
-    for (int i = tid; i < np; i += kSelThreads) s_pool[i] = a.pool_blocks[(int64_t)r * a.k_blocks + i];
+  }
+#pragma unroll
+  for (int j = 0; j < kKeysPerThread; ++j) {
+    if (base + 64 * j >= n) {
+      key[j] = 0u;
+      if (IDS) ids[j] = -1;
+    }
   }
   // count, min and max of the valid (non-zero) keys
   uint32_t nvalid = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
