@@ -135,9 +135,7 @@ def build(ctx_override=None):
 
 
 def _append(c):
-    csa2, cache = c["csa2"], c["cache"]
-    csa2.csa2_quantize_fp4(c["new_lat"], 16, cache.kv_codes, cache.kv_scales, dst_rows=c["new_dst"])
-    csa2.csa2_quantize_fp4(c["new_ik"], 32, cache.ik_codes, cache.ik_scales, dst_rows=c["new_dst"])
+    c["csa2"].csa2_cache_append(c["cache"], c["new_lat"], c["new_ik"], c["new_dst"])
 
 
 def _scan(c, l):

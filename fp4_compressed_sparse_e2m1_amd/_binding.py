@@ -56,6 +56,8 @@ def load():
         P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lib.csa2_quantize_fp4.argtypes = [P, i64, i32, i32, P, P, P, i64, P]
         lib.csa2_quantize_fp4.restype = ctypes.c_int
+        lib.csa2_cache_append.argtypes = [P, P, P, i64, P, P]
+        lib.csa2_cache_append.restype = ctypes.c_int
         lib.csa2_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         lib.csa2_workspace_size.restype = sz
         lib.csa2_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
@@ -181,6 +183,18 @@ def csa2_quantize_fp4(x, group, codes, scales, dst_rows=None, stream=None):
                                _ptr(codes, torch.uint8, "codes"), _ptr(scales, torch.uint8, "scales"),
                                rows, _stream(stream))
     _check("csa2_quantize_fp4", st)
+
+
+def csa2_cache_append(cache: Cache, latent, ikey, dst_rows, stream=None):
+    """Encodes latent fp32 [n, 512] and ikey fp32 [n, 128] into the cache's four
+    planes at plane rows dst_rows (int64 [n], seq * cap + position), one launch."""
+    n = latent.shape[0]
+    lib = load()
+    cs = cache.struct()
+    st = lib.csa2_cache_append(ctypes.byref(cs), _ptr(latent, torch.float32, "latent", (n, 512)),
+                               _ptr(ikey, torch.float32, "ikey", (n, 128)), n,
+                               _ptr(dst_rows, torch.int64, "dst_rows", (n,)), _stream(stream))
+    _check("csa2_cache_append", st)
 
 
 def csa2_index_full(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, k_blocks, k_pos,

@@ -303,6 +303,21 @@ csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t gr
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
 }
 
+csa2_status csa2_cache_append(const csa2_cache *cache, const float *latent, const float *ikey,
+                              int64_t n, const int64_t *dst_rows, void *stream) {
+  if (n < 0) return CSA2_E_INVALID_ARG;
+  if (!cache_ok(cache, true, true)) return CSA2_E_INVALID_ARG;
+  if (n == 0) return CSA2_OK;
+  if (!latent || !ikey || !dst_rows) return CSA2_E_INVALID_ARG;
+  if (!aligned(latent, 16) || !aligned(ikey, 16) || !aligned(dst_rows, 8)) return CSA2_E_INVALID_ARG;
+  if (n > ((int64_t)1 << 40) / 512) return CSA2_E_UNSUPPORTED;
+  const int64_t plane_rows = (int64_t)cache->n_seq * cache->cap;
+  hipError_t e = launch_append(latent, ikey, n, dst_rows, cache->kv_codes, cache->kv_scales,
+                               cache->ik_codes, cache->ik_scales, plane_rows,
+                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
 size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,
                            int32_t k_pos) {
   if ((op != CSA2_OP_INDEX_FULL && op != CSA2_OP_INDEX_REINDEX && op != CSA2_OP_INDEX_POOL) ||

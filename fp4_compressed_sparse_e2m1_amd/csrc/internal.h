@@ -115,5 +115,8 @@ hipError_t prepare_attention();
 // ---------------------------------------------------------------- quantise
 hipError_t launch_quantize(const float *x, int64_t n, int dim, int group, const int64_t *dst_rows,
                            uint8_t *codes, uint8_t *scales, int64_t plane_rows, hipStream_t stream);
+hipError_t launch_append(const float *lat, const float *ik, int64_t n, const int64_t *dst_rows,
+                         uint8_t *kv_codes, uint8_t *kv_scales, uint8_t *ik_codes, uint8_t *ik_scales,
+                         int64_t plane_rows, hipStream_t stream);
 
 }  // namespace csa2

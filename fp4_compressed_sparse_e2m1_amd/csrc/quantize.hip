@@ -45,22 +45,16 @@ __device__ __forceinline__ uint32_t e2m1_mag(float a, float s) {
          (uint32_t)(a > 5.0f * s);
 }
 
+// Encodes one group of G fp32 values at src into G/2 code bytes at cdst and
+// one scale byte at *sdst.
 template <int G>
-__global__ void __launch_bounds__(256)
-quantize_kernel(const float *__restrict__ x, int64_t n, int dim, const int64_t *__restrict__ dst_rows,
-                uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, int64_t plane_rows) {
-  const int ngroups = dim / G;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n * ngroups) return;
-  const int64_t r = idx / ngroups;
-  const int g = (int)(idx - r * ngroups);
-  const int64_t dst = dst_rows ? dst_rows[r] : r;
-  if (dst < 0 || dst >= plane_rows) return;
-  const float4 *src = reinterpret_cast<const float4 *>(x + r * dim + (int64_t)g * G);
+__device__ __forceinline__ void encode_group(const float *__restrict__ src, uint8_t *__restrict__ cdst,
+                                             uint8_t *__restrict__ sdst) {
+  const float4 *s4 = reinterpret_cast<const float4 *>(src);
   float v[G];
 #pragma unroll
   for (int i = 0; i < G / 4; ++i) {
-    float4 f = src[i];
+    float4 f = s4[i];
     v[4 * i] = f.x;
     v[4 * i + 1] = f.y;
     v[4 * i + 2] = f.z;
@@ -84,13 +78,52 @@ quantize_kernel(const float *__restrict__ x, int64_t n, int dim, const int64_t *
     }
     packed[w] = word;
   }
-  uint8_t *cdst = codes + dst * (dim / 2) + (int64_t)g * (G / 2);
   if constexpr (G == 16) {
     *reinterpret_cast<uint2 *>(cdst) = make_uint2(packed[0], packed[1]);
   } else {
     *reinterpret_cast<uint4 *>(cdst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   }
-  scales[dst * ngroups + g] = (uint8_t)scode;
+  *sdst = (uint8_t)scode;
+}
+
+template <int G>
+__global__ void __launch_bounds__(256)
+quantize_kernel(const float *__restrict__ x, int64_t n, int dim, const int64_t *__restrict__ dst_rows,
+                uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, int64_t plane_rows) {
+  const int ngroups = dim / G;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * ngroups) return;
+  const int64_t r = idx / ngroups;
+  const int g = (int)(idx - r * ngroups);
+  const int64_t dst = dst_rows ? dst_rows[r] : r;
+  if (dst < 0 || dst >= plane_rows) return;
+  encode_group<G>(x + r * dim + (int64_t)g * G, codes + dst * (dim / 2) + (int64_t)g * (G / 2),
+                  scales + dst * ngroups + g);
+}
+
+// Appends n entries to both planes of a cache in one launch: threads
+// [0, 32n) encode the 512-channel latents (32 groups of 16 per row), threads
+// [32n, 36n) the 128-channel indexer keys (4 groups of 32 per row).
+__global__ void __launch_bounds__(256)
+append_kernel(const float *__restrict__ lat, const float *__restrict__ ik, int64_t n,
+              const int64_t *__restrict__ dst_rows, uint8_t *__restrict__ kv_codes,
+              uint8_t *__restrict__ kv_scales, uint8_t *__restrict__ ik_codes,
+              uint8_t *__restrict__ ik_scales, int64_t plane_rows) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < n * 32) {
+    const int64_t r = idx >> 5;
+    const int g = (int)(idx & 31);
+    const int64_t dst = dst_rows[r];
+    if (dst < 0 || dst >= plane_rows) return;
+    encode_group<16>(lat + r * 512 + g * 16, kv_codes + dst * 256 + g * 8, kv_scales + dst * 32 + g);
+  } else if (idx < n * 36) {
+    const int64_t j = idx - n * 32;
+    const int64_t r = j >> 2;
+    const int g = (int)(j & 3);
+    const int64_t dst = dst_rows[r];
+    if (dst < 0 || dst >= plane_rows) return;
+    encode_group<32>(ik + r * 128 + g * 32, ik_codes + dst * 64 + g * 16, ik_scales + dst * 4 + g);
+  }
 }
 
 }  // namespace
@@ -104,6 +137,16 @@ hipError_t launch_quantize(const float *x, int64_t n, int dim, int group, const 
     quantize_kernel<16><<<blocks, 256, 0, stream>>>(x, n, dim, dst_rows, codes, scales, plane_rows);
   else
     quantize_kernel<32><<<blocks, 256, 0, stream>>>(x, n, dim, dst_rows, codes, scales, plane_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const float *lat, const float *ik, int64_t n, const int64_t *dst_rows,
+                         uint8_t *kv_codes, uint8_t *kv_scales, uint8_t *ik_codes, uint8_t *ik_scales,
+                         int64_t plane_rows, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n * 36 + 255) / 256);
+  append_kernel<<<blocks, 256, 0, stream>>>(lat, ik, n, dst_rows, kv_codes, kv_scales, ik_codes, ik_scales,
+                                            plane_rows);
   return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@
  *     "전역 어텐션과 지역 어텐션" (the 128-token SWA branch).
  *
  * A layer in each mode is a sequence of calls:
- *   Full    = csa2_quantize_fp4 (its new entries, both planes)
+ *   Full    = csa2_cache_append (its new entries, both planes; or
+ *             csa2_quantize_fp4 per plane)
  *             + csa2_index_full + csa2_sparse_attn [+ csa2_swa_merge]
  *   Reindex = csa2_index_reindex (on the Full layer's cache and pool)
  *             + csa2_sparse_attn [+ csa2_swa_merge]
@@ -125,6 +126,19 @@ typedef struct {
 csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t group,
                               const int64_t *dst_rows, uint8_t *codes, uint8_t *scales,
                               int64_t plane_rows, void *stream);
+
+/* S1 -- append new entries to a cache, both planes in one launch [the same
+ * encoding as csa2_quantize_fp4, P3 "4비트로 적어도 되는 이유"; the entry is the
+ * 288-B latent plus the 68-B indexer key, P3 "레이어 40개 가운데 4개만..."].
+ * For each i < n: latent row i (fp32 [n][512]) is encoded with group 16 into
+ * kv_codes / kv_scales row dst_rows[i], and indexer-key row i (fp32
+ * [n][128]) with group 32 into ik_codes / ik_scales row dst_rows[i]; the
+ * bytes written equal those of csa2_quantize_fp4 on each plane.  dst_rows is
+ * a device int64 [n] of plane rows (seq * cap + position); rows outside
+ * [0, n_seq * cap) are skipped.  latent and ikey must be 16-B aligned.
+ * Requires n >= 0 and a cache with all four planes. */
+csa2_status csa2_cache_append(const csa2_cache *cache, const float *latent, const float *ikey,
+                              int64_t n, const int64_t *dst_rows, void *stream);
 
 /* Scratch bytes that csa2_index_full (op CSA2_OP_INDEX_FULL),
  * csa2_index_reindex (op CSA2_OP_INDEX_REINDEX) or csa2_index_pool (op

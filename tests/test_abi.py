@@ -69,6 +69,21 @@ def test_quantize_validation():
     assert f(FAKE, 0, 512, 16, None, None, None, 0, None) == OK              # nothing to do
 
 
+def test_cache_append_validation():
+    lib = csa2.load()
+    f = lib.csa2_cache_append
+    c = cache_struct()
+    assert f(ctypes.byref(c), FAKE, FAKE, -1, FAKE, None) == INVALID           # n < 0
+    assert f(None, FAKE, FAKE, 4, FAKE, None) == INVALID                       # no cache
+    cn = cache_struct(null_ik=True)
+    assert f(ctypes.byref(cn), FAKE, FAKE, 4, FAKE, None) == INVALID           # missing plane
+    assert f(ctypes.byref(c), None, FAKE, 4, FAKE, None) == INVALID            # no latent
+    assert f(ctypes.byref(c), FAKE, FAKE, 4, None, None) == INVALID            # dst_rows required
+    assert f(ctypes.byref(c), FAKE + 4, FAKE, 4, FAKE, None) == INVALID        # misaligned latent
+    assert f(ctypes.byref(c), FAKE, FAKE + 8, 4, FAKE, None) == INVALID        # misaligned ikey
+    assert f(ctypes.byref(c), None, None, 0, None, None) == OK                 # nothing to do
+
+
 def test_index_validation():
     lib = csa2.load()
     c = cache_struct()

@@ -98,6 +98,33 @@ def test_quantize_scatter_rows(csa2):
     assert not c[untouched].any() and not s[untouched].any()
 
 
+def test_cache_append_both_planes(csa2):
+    """One launch encodes both planes exactly as the oracle (and as the
+    per-plane calls) would; rows aimed outside the planes are skipped."""
+    n_seq, cap, n = 3, 50, 21
+    lat = W.rms_rows(n, 512, seed=41).numpy()
+    ik = W.rms_rows(n, 128, seed=42).numpy()
+    lat[0] = 0.0                                   # zero groups
+    lat[1] *= 3e-5                                 # subnormal scales
+    ik[2] *= 60.0                                  # saturating scales
+    ik[3, :32] = -1e-6                             # scale underflow, negative zeros
+    rng = np.random.default_rng(5)
+    dst = rng.choice(n_seq * cap, size=n, replace=False).astype(np.int64)
+    dst[4], dst[5] = -1, n_seq * cap               # outside: skipped
+    cache = csa2.Cache(n_seq, cap)
+    csa2.csa2_cache_append(cache, dev(lat), dev(ik), dev(dst))
+    torch.cuda.synchronize()
+    kvc, kvs = oracle.quantize(lat, 16)
+    ikc, iks = oracle.quantize(ik, 32)
+    planes = [t.reshape(n_seq * cap, -1).cpu().numpy()
+              for t in (cache.kv_codes, cache.kv_scales, cache.ik_codes, cache.ik_scales)]
+    ok = (dst >= 0) & (dst < n_seq * cap)
+    for got, ref in zip(planes, (kvc, kvs, ikc, iks)):
+        np.testing.assert_array_equal(got[dst[ok]], ref[ok])
+        untouched = np.setdiff1d(np.arange(n_seq * cap), dst[ok])
+        assert not got[untouched].any()
+
+
 # ------------------------------------------------------------- S2-S4 index
 def make_index_case(csa2, n_list, cap, seed, k_rows=None):
     lat = [W.rms_rows(n, 512, seed=seed + 10 * i).numpy() for i, n in enumerate(n_list)]
