@@ -398,23 +398,34 @@ select_kernel(SelectArgs a) {
     }
   };
 
-  // Common case: the window pass.  Its histogram names the window bin that
-  // holds the k_eff-th largest key; every key at or above that bin goes, in
-  // position order, into an LDS list (about k_eff keys plus one bin), one wave
-  // resolves the remaining 13 bits on the list, and the output is compacted
-  // from the list.  Used when the keys spread beyond a plain 12-bit digit's
-  // resolution; falls back to the generic path when the k_eff-th key lies
-  // below the window or the list would overflow.
+  // Common case: one first digit, then a list.  The first digit is either a
+  // window of kSelBins bins of 2^kWinShift key units ending at the largest
+  // key (when the keys spread beyond what a plain 12-bit digit resolves that
+  // finely), or the plain digit of up to 12 bits below the highest bit in
+  // which the keys differ.  Its histogram names the bin that holds the
+  // k_eff-th largest key; every key at or above that bin goes, in position
+  // order, into an LDS list (about k_eff keys plus one bin); the remaining
+  // (at most 13) bits are resolved block-wide from the list, and the output
+  // is compacted from the list.  Falls back to the generic path when the
+  // k_eff-th key lies below the window or the list would overflow.
   bool listed = false;
-  if (k_eff < nv_all && kmin != kmax && 31 - __clz(kmin ^ kmax) > kWinShift + kSelBits - 1) {
-    const uint32_t top_bin = kmax >> kWinShift;
-    const uint32_t base_bin = top_bin >= (uint32_t)(kSelBins - 1) ? top_bin - (kSelBins - 1) : 0u;
+  if (k_eff < nv_all && kmin != kmax) {
+    const int hb = 31 - __clz(kmin ^ kmax);
+    const bool win = hb > kWinShift + kSelBits - 1;
+    const int shift0 = win ? kWinShift : (hb + 1 > kSelBits ? hb + 1 - kSelBits : 0);
+    const int width0 = win ? kSelBits : hb + 1 - shift0;
+    // first-digit bin of a key: (key >> shift0) - base_bin, in [0, 2^width0)
+    // for every valid key at or above the window (all valid keys share the
+    // bits above hb in the plain case)
+    const uint32_t top_bin = kmax >> shift0;
+    const uint32_t base_bin =
+        win ? (top_bin >= (uint32_t)(kSelBins - 1) ? top_bin - (kSelBins - 1) : 0u) : (top_bin >> width0) << width0;
 #pragma unroll
     for (int j = 0; j < kKeysPerThread; ++j)
-      if (key[j] != 0u && (key[j] >> kWinShift) >= base_bin) atomicAdd(&hist[(key[j] >> kWinShift) - base_bin], 1u);
+      if (key[j] != 0u && (key[j] >> shift0) >= base_bin) atomicAdd(&hist[(key[j] >> shift0) - base_bin], 1u);
     __syncthreads();
     if (wave == 0) {
-      const Digit d = find_digit(hist, kSelBins, k_eff, lane);
+      const Digit d = find_digit(hist, 1 << width0, k_eff, lane);
       if (lane == 0) {
         s_digit = d.digit;
         s_above = d.above;
@@ -427,7 +438,7 @@ select_kernel(SelectArgs a) {
     if (listed) {
       // bins 0 .. 191 serve the two refining passes below
       if (tid < 192) hist[tid] = 0;
-      const uint32_t lo_key = (base_bin + (uint32_t)s_digit) << kWinShift;
+      const uint32_t lo_key = (base_bin + (uint32_t)s_digit) << shift0;
       const int n_list = s_above + s_ncand;
       const unsigned long long lt = (1ull << lane) - 1ull;
       int cnt = 0;
@@ -449,9 +460,9 @@ select_kernel(SelectArgs a) {
         off += __popcll(bm);
       }
       __syncthreads();
-      // The remaining 13 bits, from the list held in registers (thread t:
-      // entries 4t .. 4t+3): bits 12..6 counted in bins 0..127, bits 5..0 in
-      // bins 128..191.
+      // The remaining shift0 (<= 13) bits, from the list held in registers
+      // (thread t: entries 4t .. 4t+3): up to 7 bits counted in bins 0..127,
+      // then the rest (<= 6) in bins 128..191.
       uint32_t lk[4];
       int32_t li[4];
 #pragma unroll
@@ -460,36 +471,46 @@ select_kernel(SelectArgs a) {
         lk[q] = e < n_list ? s_lkey[e] : 0u;
         li[q] = e < n_list ? s_lid[e] : -1;
       }
+      const int wA = shift0 < 7 ? shift0 : 7;
+      const int sA = shift0 - wA;
       uint32_t prefix = lo_key;
       int k_rem = k_eff - s_above;
+      if (wA > 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lk[q] != 0u && (lk[q] >> kWinShift) == (prefix >> kWinShift)) atomicAdd(&hist[(lk[q] >> 6) & 127u], 1u);
-      __syncthreads();
-      if (wave == 0) {
-        const Digit d = find_digit(hist, 128, k_rem, lane);
-        if (lane == 0) {
-          s_digit = d.digit;
-          s_above = d.above;
+        for (int q = 0; q < 4; ++q)
+          if (lk[q] != 0u && (lk[q] >> shift0) == (prefix >> shift0))
+            atomicAdd(&hist[(lk[q] >> sA) & ((1u << wA) - 1u)], 1u);
+        __syncthreads();
+        if (wave == 0) {
+          const Digit d = find_digit(hist, 1 << wA, k_rem, lane);
+          if (lane == 0) {
+            s_digit = d.digit;
+            s_above = d.above;
+          }
         }
+        __syncthreads();
+        prefix |= (uint32_t)s_digit << sA;
+        k_rem -= s_above;
       }
-      __syncthreads();
-      prefix |= (uint32_t)s_digit << 6;
-      k_rem -= s_above;
+      if (sA > 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lk[q] != 0u && (lk[q] >> 6) == (prefix >> 6)) atomicAdd(&hist[128 + (lk[q] & 63u)], 1u);
-      __syncthreads();
-      if (wave == 0) {
-        const Digit d = find_digit(hist + 128, 64, k_rem, lane);
-        if (lane == 0) {
-          s_thr = prefix | (uint32_t)d.digit;
-          s_keq = k_rem - d.above;
+        for (int q = 0; q < 4; ++q)
+          if (lk[q] != 0u && (lk[q] >> sA) == (prefix >> sA)) atomicAdd(&hist[128 + (lk[q] & ((1u << sA) - 1u))], 1u);
+        __syncthreads();
+        if (wave == 0) {
+          const Digit d = find_digit(hist + 128, 1 << sA, k_rem, lane);
+          if (lane == 0) {
+            s_digit = d.digit;
+            s_above = d.above;
+          }
         }
+        __syncthreads();
+        prefix |= (uint32_t)s_digit;
+        k_rem -= s_above;
       }
-      __syncthreads();
-      const uint32_t thr = s_thr;
-      const int k_eq = s_keq;
+      // every thread has followed the same digits
+      const uint32_t thr = prefix;
+      const int k_eq = k_rem;
       // ordered compaction of the list; above-threshold and tie counts
       // travel packed in one prefix sum
       int packed = 0;
