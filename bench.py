@@ -48,9 +48,9 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "38fc0fb280ef78d261a1a8ed9f799b3007cb130b9c9027e9573265f99ee2fdb0",
-    "fetch_kib": 278651.198, "fetch_scale": 524288 / 262166.875,
-    "write_kib": 4325.568, "write_scale": 524288 / 524288.0,
+    "sha256": "b14307a55fe5f7c1d288c895d64968a0187fb6a0894bb63787ef1d71aba97e2e",
+    "fetch_kib": 278648.885, "fetch_scale": 524288 / 262166.75,
+    "write_kib": 4172.156, "write_scale": 524288 / 524288.0,
 }
 
 
