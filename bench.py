@@ -48,7 +48,7 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "b14307a55fe5f7c1d288c895d64968a0187fb6a0894bb63787ef1d71aba97e2e",
+    "sha256": "9d542c5da7091519d19c0441fbb8e0c78f5c40f161ccb1deb29d482a0a7c29a1",
     "fetch_kib": 278648.885, "fetch_scale": 524288 / 262166.75,
     "write_kib": 4172.156, "write_scale": 524288 / 524288.0,
 }

@@ -22,14 +22,19 @@
 // accumulate in fp32.
 //
 // Selection: scores are mapped to order-preserving uint32 keys (0 = no
-// candidate).  A work-group holds up to 16,384 keys of one row in registers
-// (16 per thread) and runs an 8-bit radix select for the k-th largest key,
-// starting at the highest bit in which its keys differ, with LDS histograms;
-// once the keys still in play fit in LDS, one wave finishes the digits alone.
-// An ordered compaction (ballot prefix counts) then writes the kept positions
-// in ascending order, ties at the threshold going to the lowest positions.  Rows with more keys are cut into
-// chunks whose Top-k survivors feed a further level, which keeps the result
-// exact because a global Top-k element is in its chunk's Top-k.
+// candidate).  A 1,024-thread work-group holds up to 16,384 keys of one row in
+// registers (16 per thread).  One LDS histogram of up to 4,096 bins over the
+// first digit -- a window ending at the largest key, or the plain digit below
+// the highest bit in which the keys differ -- names the bin holding the k-th
+// key; the keys at or above that bin are gathered, in position order with
+// their ids, into an LDS list; the remaining bits are resolved from the list
+// and the output is compacted from it, ties at the threshold going to the
+// lowest positions.  A generic radix path (12-bit digits, then one wave on the
+// keys still in play, then a ballot-ordered compaction from registers) covers
+// the cases the list cannot hold.  Rows with more keys are cut into chunks
+// whose Top-k survivors feed a further level, which keeps the result exact
+// because a global Top-k element is in its chunk's Top-k.
+
 #include "device.h"
 #include "internal.h"
 
