@@ -333,7 +333,7 @@ def test_sparse_attn_global_fused_and_merge(csa2, H, split):
     ws_g = csa2.attn_workspace(R, H, k_pos, 0) if split else None
     ws_m = csa2.attn_workspace(R, H, 0, 128) if split else None
     ws_f = csa2.attn_workspace(R, H, k_pos, 128) if split else None
-    if split and H > 16:       # 16 heads split keys inside one work-group and need none
+    if split:                  # few rows: every branch spreads over work-groups
         assert ws_g is not None and ws_m is not None and ws_f is not None
     # global branch only
     o = torch.empty((R, H, 512), device="cuda")
@@ -354,6 +354,38 @@ def test_sparse_attn_global_fused_and_merge(csa2, H, split):
     torch.cuda.synchronize()
     check_attention(o2.cpu().numpy(), lse2.cpu().numpy(), np.stack([x["o"] for x in refs]),
                     np.stack([x["lse"] for x in refs]), "fused")
+
+
+@pytest.mark.parametrize("H,n_rows,k_pos,window,split", [
+    (32, 3, 97, 100, True),       # 32 heads; Top-K and window not multiples of the 32-key tile
+    (32, 3, 97, 100, False),
+    (16, 1, 2048, 1024, True),    # 96 tiles over 48 work-groups: the merge's loop past 16 splits
+    (64, 200, 64, 32, True),      # 200 rows: no split even with a workspace requested
+    (16, 5, 33, 1, True),         # one-row window, a 1-key second tile
+], ids=["h32_ragged_split", "h32_ragged", "h16_2048_1024_48splits", "h64_200rows", "h16_tiny_tiles"])
+def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
+    rng = np.random.default_rng(k_pos + window)
+    n_vis = max(3000, k_pos + 10)
+    rows = []
+    for r in range(n_rows):
+        cnt = k_pos if r % 3 == 0 else int(rng.integers(0, k_pos + 1))
+        rows.append((np.sort(rng.choice(n_vis, cnt, replace=False)), 0))
+    swa_len = window + 50
+    ends = [swa_len if r % 2 == 0 else int(rng.integers(0, swa_len + 1)) for r in range(n_rows)]
+    c = attn_case(csa2, H, [n_vis], rows, swa_ends=ends, seed=H + window, swa_len=swa_len, window=window)
+    assert c["topk"].shape[1] == k_pos
+    ws = csa2.attn_workspace(n_rows, H, k_pos, window) if split else None
+    if split:
+        assert (ws is None) == (n_rows >= 192)
+    swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), window)
+    o = torch.empty((n_rows, H, 512), device="cuda")
+    lse = torch.empty((n_rows, H), device="cuda")
+    csa2.csa2_sparse_attn(c["cache"], dev(c["q"]), dev(c["row_seq"]), dev(c["topk"]), dev(c["ntopk"]),
+                          SCALE, o, lse, swa=swa, workspace=ws)
+    torch.cuda.synchronize()
+    refs = [oracle_attn(c, r) for r in range(n_rows)]
+    check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o"] for x in refs]),
+                    np.stack([x["lse"] for x in refs]), f"H{H} k{k_pos} w{window}")
 
 
 @pytest.mark.parametrize("split", [False, True])
