@@ -417,8 +417,9 @@ attn_merge_kernel(AttnArgs a, int H) {
   const int h = h0 + hh;
   const float *po = a.part_o + (((int64_t)r * ns) * H + h) * 512 + d;
   // The first (up to) kMergeBatch splits' partials are requested before the
-  // weights are known, so their loads overlap the weight computation.
-  constexpr int kMergeBatch = 16;
+  // weights are known, so their loads overlap the weight computation; further
+  // splits are read in batches of the same size.
+  constexpr int kMergeBatch = 32;
   float4 v[kMergeBatch];
 #pragma unroll
   for (int u = 0; u < kMergeBatch; ++u)
@@ -471,13 +472,20 @@ attn_merge_kernel(AttnArgs a, int H) {
       acc.w += wgt * v[u].w;
     }
   }
-  for (int s = kMergeBatch; s < ns; ++s) {
-    const float4 x = *reinterpret_cast<const float4 *>(po + (int64_t)s * H * 512);
-    const float wgt = s_w[hh][s];
-    acc.x += wgt * x.x;
-    acc.y += wgt * x.y;
-    acc.z += wgt * x.z;
-    acc.w += wgt * x.w;
+  for (int s0 = kMergeBatch; s0 < ns; s0 += kMergeBatch) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (s0 + u < ns) v[u] = *reinterpret_cast<const float4 *>(po + (int64_t)(s0 + u) * H * 512);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (s0 + u < ns) {
+        const float wgt = s_w[hh][s0 + u];
+        acc.x += wgt * v[u].x;
+        acc.y += wgt * v[u].y;
+        acc.z += wgt * v[u].z;
+        acc.w += wgt * v[u].w;
+      }
+    }
   }
   float4 *orow = reinterpret_cast<float4 *>(a.o + ((int64_t)r * H + h) * 512 + d);
   const float win = s_w[hh][ns];
@@ -503,14 +511,13 @@ AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t 
   const int max_tiles = (k_pos + kTileKeys - 1) / kTileKeys + (window + kTileKeys - 1) / kTileKeys;
   AttnPlan p = {1, max_tiles > 0 ? max_tiles : 1, 0};
   // Few rows leave most of the 256 CUs idle: spread each row's key tiles over
-  // several work-groups (about 256 in all, at least two tiles each).  Many rows
-  // fill the GPU already, and splitting them would only add partial-result
-  // traffic.
-  if (n_rows >= 192 || max_tiles <= 2) return p;
+  // several work-groups (about 256 in all; one tile each when that many
+  // fit).  Many rows fill the GPU already, and splitting them would only add
+  // partial-result traffic.
+  if (n_rows >= 192 || max_tiles <= 1) return p;
   int split = (256 + n_rows - 1) / n_rows;
   split = split < max_tiles ? split : max_tiles;
   int tps = (max_tiles + split - 1) / split;
-  tps = tps < 2 ? 2 : tps;                 // at least two tiles, so loads overlap compute
   split = (max_tiles + tps - 1) / tps;
   split = split < kMergeSplitLimit ? split : kMergeSplitLimit;
   tps = (max_tiles + split - 1) / split;
