@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=8,
                     help="query rows of the step the oracle runs for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attention-roofline", action="store_true",
+                    help="skip the batch-256, 64-head attention bandwidth measurement")
     ap.add_argument("--ctx", type=int, default=None, help="override the context (testing only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB buffer once with a plain device copy "
@@ -273,6 +275,85 @@ class _NoEvent:
         pass
 
 
+def reuse_attention(steps, warmup):
+    """The attention kernel where it carries enough bytes to be bandwidth-bound:
+    one Reuse layer at batch 256, 64 heads, contexts U[64K, 256K] entries, an
+    inherited uniform Top-512 per row and a 128-row FP8 SWA window, fused in
+    one softmax.  Algorithmic bytes per query: 512 x 288 (gathered latents) +
+    128 x 512 (SWA) + 64 x 1,024 (q) + 512 x 4 (ids) + 64 x 2,048 (o) + 64 x 4
+    (lse) = 411,904 B."""
+    import torch
+
+    import fp4_compressed_sparse_e2m1_amd as csa2
+    import workloads as W
+
+    wl = W.WORKLOADS[4]
+    B, H, seed = wl.batch, wl.heads, wl.seed
+    lens = W.lengths_uniform(B, wl.ctx_min, wl.ctx, W.seed_for(seed, W.T_LEN))
+    cap = int(lens.max())
+    cache = csa2.Cache(B, cap)
+    for s in range(B):
+        n = int(lens[s])
+        lat = W.rms_rows(n, 512, W.seed_for(seed, W.T_LATENT, 0, s), device="cuda")
+        dst = torch.arange(n, dtype=torch.int64, device="cuda") + s * cap
+        csa2.csa2_quantize_fp4(lat, 16, cache.kv_codes, cache.kv_scales, dst_rows=dst)
+        del lat, dst
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    topk = torch.stack([torch.from_numpy(W.topk_uniform(int(lens[s]), wl.k_pos,
+                                                        W.seed_for(seed, W.T_TOPK, 0, s)).astype("int32"))
+                        for s in range(B)]).cuda()
+    ntopk = i32([wl.k_pos] * B)
+    swa = csa2.Swa(W.swa_rows_e4m3(B * wl.swa, 512, W.seed_for(seed, W.T_SWA), device="cuda")
+                   .reshape(B, wl.swa, 512), i32([wl.swa] * B), wl.swa)
+    q = W.bf16_normal((B, H, 512), W.seed_for(seed, W.T_Q), device="cuda")
+    seqs = i32(list(range(B)))
+    o = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = csa2.attn_workspace(B, H, wl.k_pos, wl.swa)
+
+    def run():
+        csa2.csa2_sparse_attn(cache, q, seqs, topk, ntopk, SCALE, o, lse, swa=swa, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    per_query = 512 * 288 + wl.swa * 512 + H * 1024 + 512 * 4 + H * 2048 + H * 4
+    achieved = per_query * B / (us * 1e-6) / 1e9
+    del cache
+    return {"workload": wl.name, "kernel": "attn_kernel<64 heads> (csa2_sparse_attn, SWA fused)",
+            "avg_launch_us": round(us, 2), "query_tokens_per_s": round(B / (us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": per_query * B}}
+
+
+def copy_bandwidth():
+    """A plain 1-GiB device-to-device copy on this GPU (read + write bytes / time)."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    del src, dst
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(c, rows):
     """The oracle, as it stands, on `rows` query rows of the same step (all 20
     layers, full 1M context), one host thread per row.  The oracle builds its
@@ -417,6 +498,9 @@ def main():
         "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
         "build_s": round(t_build, 1),
     }
+    line["hbm_copy_GBs"] = copy_bandwidth()
+    if not args.no_attention_roofline:
+        line["attention_b256_h64"] = reuse_attention(20, 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
     print(json.dumps(line), flush=True)
