@@ -8,15 +8,20 @@
 // The latent is shared by all heads and is both key and value (one latent per
 // entry, no separate V in the 356-B entry).
 //
-// One work-group (4 waves) handles one query row and all of its heads.  Keys
-// are consumed in tiles of 32 (two blocks of 16).  Wave w owns the channel
-// quarter [128w, 128w+128):
+// One work-group (4 waves) handles one query row (or one split of its keys)
+// and a group of 16 heads (16-head layers) or 32 heads (32- and 64-head
+// layers; a 64-head row takes two work-groups, given block ids that place
+// both on one XCD so the gathered keys come from its L2 once).  Keys are
+// consumed in tiles of 32 (two blocks of 16): the Top-K tiles first, with the
+// ids read and the gathers issued two tiles ahead, then the SWA tiles.  Wave w
+// owns the channel quarter [128w, 128w+128):
 //   * it gathers only its quarter of each key (16 B of E2M1 codes + 2 scale
 //     bytes, or 32 B of E4M3 for SWA rows) and dequantises it once, exactly,
 //     to f16;
 //   * Q.K^T: it computes the partial logits over its quarter with 16x16x32
 //     MFMAs (rows = 16 heads, columns = 16 keys); the four partials are summed
-//     through LDS;
+//     through LDS ([head][key] rows, so the writes and the softmax reads are
+//     free of bank conflicts);
 //   * P.V: it keeps its dequantised quarter in LDS (natural layout) and
 //     accumulates O[:, quarter] with MFMAs (rows = 16 heads, columns = 16
 //     channels, contraction = the 32 keys of the tile), reading the V
@@ -34,14 +39,23 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kTileKeys = kAttnTileKeys;
 constexpr int kMergeSplitLimit = 64;     // splits the merge kernel accepts
-constexpr int kVnStride = 128 + 16;    // halves per LDS key row: a wave's 128 channels + pad
+constexpr int kVnStride = 128 + 8;     // halves per LDS key row: a wave's 128 channels + pad
+                                       // (16-B writes of 16 rows land on distinct banks)
 constexpr int kPStride = 40;           // halves per P row
+constexpr int kSPStride = 32 + 4;      // floats per partial-logit row (one head, 32 keys + pad)
 constexpr float kLazyRescale = 8.0f;   // log2 units
 
-struct RawTile {
-  uint4 a[2];       // FP4: codes of the quarter; SWA: bytes 0..15 of the quarter
-  uint4 b[2];       // SWA: bytes 16..31
-  uint32_t sc[2];   // FP4: two scale bytes
+// One wave's raw share of a 32-key tile (two 16-key blocks kb): FP4 codes of
+// its channel quarter plus two scale bytes per key, or 32 E4M3 bytes per key
+// of an SWA row.
+struct Fp4Tile {
+  uint4 a[2];
+  uint32_t sc[2];
+  bool valid[2];
+};
+struct SwaTile {
+  uint4 a[2];       // bytes 0..15 of the lane's 32
+  uint4 b[2];       // bytes 16..31
   bool valid[2];
 };
 
@@ -67,20 +81,38 @@ __device__ __forceinline__ float group_sum(float x) {
 template <int HB>
 __global__ void __launch_bounds__(kAttnThreads)
 attn_kernel(AttnArgs a) {
-  static_assert(HB == 1 || HB == 2 || HB == 4, "heads must be 16, 32 or 64");
+  static_assert(HB == 1 || HB == 2, "a work-group takes 16 or 32 heads");
   constexpr int H = 16 * HB;
   constexpr int TPH = kAttnThreads / H;        // softmax threads per head
   constexpr int KPT = kTileKeys / TPH;         // keys per softmax thread
 
-  __shared__ __attribute__((aligned(16))) float s_part[4][kTileKeys][H];
+  // partial logits, [wave][head][key]: the MFMA result goes out as single
+  // words with consecutive keys in consecutive banks, and each softmax thread
+  // reads its keys of one head contiguously
+  __shared__ __attribute__((aligned(16))) float s_part[4][H][kSPStride];
   __shared__ __attribute__((aligned(16))) _Float16 s_vn[4][kTileKeys * kVnStride];
   __shared__ __attribute__((aligned(16))) _Float16 s_p[H * kPStride];
   __shared__ __attribute__((aligned(16))) float s_alpha[H];
   __shared__ float s_m[H], s_l[H];
   __shared__ int s_valid[kTileKeys];
 
-  const int r = blockIdx.x / a.n_split;
-  const int sp = blockIdx.x - r * a.n_split;
+  // Work-group -> (row, split, head group).  With several head groups, the
+  // groups of one (row, split) get block ids equal modulo 8, so they run on
+  // one XCD (work-groups go to the 8 XCDs in turn) and share its L2 for the
+  // gathered keys; the grid is padded to whole sets of 8.
+  const int HT = a.n_heads;
+  int rs = blockIdx.x, hg = 0;
+  if (a.n_hgroups > 1) {
+    const int per = 8 * a.n_hgroups;
+    const int blk = blockIdx.x / per;
+    const int rem = blockIdx.x - blk * per;
+    hg = rem >> 3;
+    rs = blk * 8 + (rem & 7);
+  }
+  if (rs >= a.n_rows * a.n_split) return;
+  const int h0 = hg * H;
+  const int r = rs / a.n_split;
+  const int sp = rs - r * a.n_split;
   const bool split = a.n_split > 1;
   const bool merge_in = a.merge_in && !split;   // with a split the merge kernel folds (o, lse) in
   const int tid = threadIdx.x;
@@ -111,11 +143,11 @@ attn_kernel(AttnArgs a) {
   int t_end = split ? t_begin + a.tiles_per_split : n_all;
   t_end = t_end < n_all ? t_end : n_all;
 
-  // Q operand: qa[hb][t] = q[r][16hb + c][128w + 32G + 8t .. +7] in f16.
+  // Q operand: qa[hb][t] = q[r][h0 + 16hb + c][128w + 32G + 8t .. +7] in f16.
   f16x8 qa[HB][4];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * H + 16 * hb + c) * 512 +
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * HT + h0 + 16 * hb + c) * 512 +
                                                       128 * w + 32 * G);
 #pragma unroll
     for (int t = 0; t < 4; ++t) qa[hb][t] = bf16x8_to_f16(qp[t]);
@@ -134,11 +166,11 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 16 * hb + 4 * G + i;
-        const float lin = a.lse[(int64_t)r * H + h];
+        const float lin = a.lse[(int64_t)r * HT + h0 + h];
         if (lin != -INFINITY) {
 #pragma unroll
           for (int db = 0; db < 8; ++db)
-            acc_o[hb][db][i] = a.o[((int64_t)r * H + h) * 512 + 128 * w + 16 * db + c];
+            acc_o[hb][db][i] = a.o[((int64_t)r * HT + h0 + h) * 512 + 128 * w + 16 * db + c];
         }
       }
   }
@@ -147,7 +179,7 @@ attn_kernel(AttnArgs a) {
   // the normaliser as per-thread partial sums, reduced once at the end.
   float m_run = -INFINITY, l_thr = 0.f;
   if (merge_in) {
-    const float lin = a.lse[(int64_t)r * H + tid / TPH];
+    const float lin = a.lse[(int64_t)r * HT + h0 + tid / TPH];
     if (lin != -INFINITY) {
       m_run = lin * 1.4426950408889634f;
       l_thr = (tid % TPH) == 0 ? 1.f : 0.f;
@@ -170,77 +202,85 @@ attn_kernel(AttnArgs a) {
       e[kb] = (topk && slot < a.k_pos) ? topk[slot] : -1;
     }
   };
-  auto load_tile = [&](int tile, const int32_t (&ids)[2]) {
-    RawTile t;
-    if (tile < n_gt) {
+  auto load_fp4 = [&](int tile, const int32_t (&ids)[2]) {
+    Fp4Tile t;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int slot = tile * kTileKeys + 16 * kb + c;
-        const int64_t e = slot < n_g ? ids[kb] : -1;
-        const bool ok = e >= 0 && e < a.cap;
-        t.valid[kb] = ok;
-        const int64_t el = ok ? e : 0;
-        t.a[kb] = *reinterpret_cast<const uint4 *>(kv_codes + el * 256 + 64 * w + 16 * G);
-        t.sc[kb] = *reinterpret_cast<const uint16_t *>(kv_scales + el * 32 + 8 * w + 2 * G);
-        t.b[kb] = make_uint4(0, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int slot = (tile - n_gt) * kTileKeys + 16 * kb + c;
-        const bool ok = slot < n_s;
-        t.valid[kb] = ok;
-        const int64_t row = ok ? s0 + slot : 0;
-        const uint4 *p = reinterpret_cast<const uint4 *>(swa + row * 512 + 128 * w + 32 * G);
-        t.a[kb] = p[0];
-        t.b[kb] = p[1];
-        t.sc[kb] = 0;
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const int slot = tile * kTileKeys + 16 * kb + c;
+      const int64_t e = slot < n_g ? ids[kb] : -1;
+      const bool ok = e >= 0 && e < a.cap;
+      t.valid[kb] = ok;
+      const int64_t el = ok ? e : 0;
+      t.a[kb] = *reinterpret_cast<const uint4 *>(kv_codes + el * 256 + 64 * w + 16 * G);
+      t.sc[kb] = *reinterpret_cast<const uint16_t *>(kv_scales + el * 32 + 8 * w + 2 * G);
     }
     return t;
   };
-
-  // the first two tiles' ids are read before n_topk arrives (t_begin does
-  // not depend on it); slots past the row's count are masked in load_tile
-  int32_t ids_cur[2], ids_nxt[2];
-  load_ids(t_begin, ids_cur);
-  load_ids(t_begin + 1, ids_nxt);
-  RawTile ta, tb;
-  if (t_begin < t_end) ta = load_tile(t_begin, ids_cur);
-
-  // One tile: dequantise, partial logits, online softmax, P.V.
-  auto compute_tile = [&](const RawTile &cur, int tile) {
-    const bool is_swa = tile >= n_gt;
-
-    // dequantise this wave's quarter of the 32 keys
-    f16x8 kf[2][4];
+  auto load_swa = [&](int tile) {   // tile index within the SWA rows
+    SwaTile t;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      if (!is_swa) {
-        const _Float16 sa = e4m3_to_f16(cur.sc[kb] & 0xFFu);
-        const _Float16 sb = e4m3_to_f16((cur.sc[kb] >> 8) & 0xFFu);
-        const f16x8 va = f16x8{sa, sa, sa, sa, sa, sa, sa, sa};
-        const f16x8 vb = f16x8{sb, sb, sb, sb, sb, sb, sb, sb};
-        kf[kb][0] = e2m1x8_to_f16(cur.a[kb].x) * va;
-        kf[kb][1] = e2m1x8_to_f16(cur.a[kb].y) * va;
-        kf[kb][2] = e2m1x8_to_f16(cur.a[kb].z) * vb;
-        kf[kb][3] = e2m1x8_to_f16(cur.a[kb].w) * vb;
-      } else {
-        kf[kb][0] = e4m3x8_to_f16(cur.a[kb].x, cur.a[kb].y);
-        kf[kb][1] = e4m3x8_to_f16(cur.a[kb].z, cur.a[kb].w);
-        kf[kb][2] = e4m3x8_to_f16(cur.b[kb].x, cur.b[kb].y);
-        kf[kb][3] = e4m3x8_to_f16(cur.b[kb].z, cur.b[kb].w);
-      }
-      if (!cur.valid[kb]) {
-        // skipped slots load entry 0; zero them so no stale byte pattern
-        // (e.g. a NaN code in an unwritten row) can reach the P.V product
+      const int slot = tile * kTileKeys + 16 * kb + c;
+      const bool ok = slot < n_s;
+      t.valid[kb] = ok;
+      const int64_t row = ok ? s0 + slot : 0;
+      const uint4 *p = reinterpret_cast<const uint4 *>(swa + row * 512 + 128 * w + 32 * G);
+      t.a[kb] = p[0];
+      t.b[kb] = p[1];
+    }
+    return t;
+  };
+  // dequantise a wave's quarter of a tile's 32 keys to f16 (exact); skipped
+  // slots load entry 0 and are zeroed, so no stale byte pattern (e.g. a NaN
+  // code in an unwritten row) can reach the P.V product
+  auto dequant_fp4 = [&](const Fp4Tile &t, f16x8 (&kf)[2][4]) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) kf[kb][t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kb = 0; kb < 2; ++kb) {
+      const _Float16 sa = e4m3_to_f16(t.sc[kb] & 0xFFu);
+      const _Float16 sb = e4m3_to_f16((t.sc[kb] >> 8) & 0xFFu);
+      const f16x8 va = f16x8{sa, sa, sa, sa, sa, sa, sa, sa};
+      const f16x8 vb = f16x8{sb, sb, sb, sb, sb, sb, sb, sb};
+      kf[kb][0] = e2m1x8_to_f16(t.a[kb].x) * va;
+      kf[kb][1] = e2m1x8_to_f16(t.a[kb].y) * va;
+      kf[kb][2] = e2m1x8_to_f16(t.a[kb].z) * vb;
+      kf[kb][3] = e2m1x8_to_f16(t.a[kb].w) * vb;
+      if (!t.valid[kb]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kf[kb][q] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
+  };
+  auto dequant_swa = [&](const SwaTile &t, f16x8 (&kf)[2][4]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      kf[kb][0] = e4m3x8_to_f16(t.a[kb].x, t.a[kb].y);
+      kf[kb][1] = e4m3x8_to_f16(t.a[kb].z, t.a[kb].w);
+      kf[kb][2] = e4m3x8_to_f16(t.b[kb].x, t.b[kb].y);
+      kf[kb][3] = e4m3x8_to_f16(t.b[kb].z, t.b[kb].w);
+      if (!t.valid[kb]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kf[kb][q] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  };
+
+  // the first three global tiles' ids are read before n_topk arrives
+  // (t_begin does not depend on it); slots past the row's count are masked in
+  // load_fp4
+  int32_t id0[2], id1[2], id2[2];
+  load_ids(t_begin, id0);
+  load_ids(t_begin + 1, id1);
+  load_ids(t_begin + 2, id2);
+  const int g_end = t_end < n_gt ? t_end : n_gt;      // global tiles: [t_begin, g_end)
+  Fp4Tile ta, tb, tc;
+  if (t_begin < g_end) ta = load_fp4(t_begin, id0);
+  if (t_begin + 1 < g_end) tb = load_fp4(t_begin + 1, id1);
+
+  // One tile of dequantised keys: partial logits, online softmax, P.V.
+  auto compute_tile = [&](const f16x8 (&kf)[2][4], const bool (&valid)[2]) {
     if (w == 0 && G == 0) {
-      s_valid[c] = cur.valid[0];
-      s_valid[16 + c] = cur.valid[1];
+      s_valid[c] = valid[0];
+      s_valid[16 + c] = valid[1];
     }
 
     // partial logits over this wave's channel quarter
@@ -251,8 +291,8 @@ attn_kernel(AttnArgs a) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) s = mfma16x16x32(qa[hb][t], kf[kb][t], s);
-        *reinterpret_cast<float4 *>(&s_part[w][16 * kb + c][16 * hb + 4 * G]) =
-            make_float4(s[0], s[1], s[2], s[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_part[w][16 * hb + 4 * G + i][16 * kb + c] = s[i];
       }
     // this wave's dequantised quarter, natural layout [key][channel]; the P.V
     // product reads it back transposed
@@ -273,7 +313,7 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int kk = kk0 + j;
-        float s = (s_part[0][kk][h] + s_part[1][kk][h]) + (s_part[2][kk][h] + s_part[3][kk][h]);
+        float s = (s_part[0][h][kk] + s_part[1][h][kk]) + (s_part[2][h][kk] + s_part[3][h][kk]);
         s = s_valid[kk] ? s * a.scale_log2 : -INFINITY;
         sv[j] = s;
         tmax = fmaxf(tmax, s);
@@ -281,15 +321,19 @@ attn_kernel(AttnArgs a) {
       tmax = group_max<TPH>(tmax);
       float m_new = m_run;
       if (m_run == -INFINITY || tmax > m_run + kLazyRescale) m_new = fmaxf(tmax, m_run);
-      const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+      // the hardware exp2 (no denormal-range fix-up): arguments are <= 2^8,
+      // and results below 2^-126 are negligible weights (f16 drops them too)
+      const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       float psum = 0.f;
+      _Float16 ph[KPT];
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const float p = (m_new == -INFINITY) ? 0.f : exp2f(sv[j] - m_new);
-        const _Float16 ph = (_Float16)p;
-        s_p[h * kPStride + kk0 + j] = ph;
-        psum += (float)ph;
+        const float p = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_new);
+        ph[j] = (_Float16)p;
+        psum += (float)ph[j];
       }
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) s_p[h * kPStride + kk0 + j] = ph[j];
       l_thr = l_thr * alpha + psum;
       m_run = m_new;
       if ((tid % TPH) == 0) s_alpha[h] = alpha;
@@ -315,40 +359,55 @@ attn_kernel(AttnArgs a) {
     // B operand of channel block db: keys 8G .. 8G+7 at channel 16db + c.
     // Lane (G, c) addresses row 8G + 4h + c/4, channels 16db + 4 (c % 4) of
     // the two 4-key halves h.
-    f16x8 vb[8];
-    {
-      const _Float16 *r0 = vn + (8 * G + (c >> 2)) * kVnStride + 4 * (c & 3);
-      const _Float16 *r1 = r0 + 4 * kVnStride;
+    // (read two channel blocks at a time, to bound the registers they hold)
+    const _Float16 *r0 = vn + (8 * G + (c >> 2)) * kVnStride + 4 * (c & 3);
+    const _Float16 *r1 = r0 + 4 * kVnStride;
+    f16x8 pa[HB];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const f16x4 lo = lds_read_tr16(r0 + 16 * db);
-        const f16x4 hi = lds_read_tr16(r1 + 16 * db);
-        vb[db] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int hb = 0; hb < HB; ++hb) pa[hb] = *reinterpret_cast<const f16x8 *>(&s_p[(16 * hb + c) * kPStride + 8 * G]);
+#pragma unroll
+    for (int db = 0; db < 8; db += 2) {
+      f16x8 vb[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f16x4 lo = lds_read_tr16(r0 + 16 * (db + u));
+        const f16x4 hi = lds_read_tr16(r1 + 16 * (db + u));
+        vb[u] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-    }
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const f16x8 pa = *reinterpret_cast<const f16x8 *>(&s_p[(16 * hb + c) * kPStride + 8 * G]);
+      for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) acc_o[hb][db] = mfma16x16x32(pa, vb[db], acc_o[hb][db]);
+        for (int u = 0; u < 2; ++u) acc_o[hb][db + u] = mfma16x16x32(pa[hb], vb[u], acc_o[hb][db + u]);
     }
     __syncthreads();
   };
 
-  // Two tiles per trip with alternating registers, so the prefetched tile is
-  // never copied into the current one.
-  for (int tile = t_begin; tile < t_end; tile += 2) {
-    if (tile + 1 < t_end) tb = load_tile(tile + 1, ids_nxt);
-    int32_t ids_n2[2] = {-1, -1};
-    if (tile + 2 < t_end) load_ids(tile + 2, ids_n2);
-    compute_tile(ta, tile);
-    if (tile + 1 >= t_end) break;
-    if (tile + 2 < t_end) ta = load_tile(tile + 2, ids_n2);
-    int32_t ids_n3[2] = {-1, -1};
-    if (tile + 3 < t_end) load_ids(tile + 3, ids_n3);
-    compute_tile(tb, tile + 1);
-    ids_nxt[0] = ids_n3[0];
-    ids_nxt[1] = ids_n3[1];
+  // Global tiles: while a tile is computed the next two are in flight (the
+  // gathers are random HBM reads); the three tile registers rotate by copy.
+  f16x8 kf[2][4];
+  for (int tile = t_begin; tile < g_end; ++tile) {
+    int32_t idn[2] = {-1, -1};
+    if (tile + 2 < g_end) tc = load_fp4(tile + 2, id2);
+    if (tile + 3 < g_end) load_ids(tile + 3, idn);
+    dequant_fp4(ta, kf);
+    compute_tile(kf, ta.valid);
+    ta = tb;
+    tb = tc;
+    id2[0] = idn[0];
+    id2[1] = idn[1];
+  }
+  // SWA tiles (consecutive rows), the next one in flight
+  {
+    const int sw_begin = (t_begin > n_gt ? t_begin : n_gt) - n_gt;
+    const int sw_end = t_end - n_gt;
+    SwaTile sa, sb;
+    if (sw_begin < sw_end) sa = load_swa(sw_begin);
+    for (int st = sw_begin; st < sw_end; ++st) {
+      if (st + 1 < sw_end) sb = load_swa(st + 1);
+      dequant_swa(sa, kf);
+      compute_tile(kf, sa.valid);
+      sa = sb;
+    }
   }
 
   {
@@ -367,13 +426,13 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 16 * hb + 4 * G + i;
-        float *prow = a.part_o + (part * H + h) * 512 + 128 * w + c;
+        float *prow = a.part_o + (part * HT + h0 + h) * 512 + 128 * w + c;
 #pragma unroll
         for (int db = 0; db < 8; ++db) prow[16 * db] = acc_o[hb][db][i];
       }
     if (tid < H) {
-      a.part_ml[(part * H + tid) * 2] = s_m[tid];
-      a.part_ml[(part * H + tid) * 2 + 1] = s_l[tid];
+      a.part_ml[(part * HT + h0 + tid) * 2] = s_m[tid];
+      a.part_ml[(part * HT + h0 + tid) * 2 + 1] = s_l[tid];
     }
     return;
   }
@@ -385,14 +444,14 @@ attn_kernel(AttnArgs a) {
       const int h = 16 * hb + 4 * G + i;
       const float l = s_l[h];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      float *orow = a.o + ((int64_t)r * H + h) * 512 + 128 * w + c;
+      float *orow = a.o + ((int64_t)r * HT + h0 + h) * 512 + 128 * w + c;
 #pragma unroll
       for (int db = 0; db < 8; ++db) orow[16 * db] = acc_o[hb][db][i] * inv;
     }
   }
   if (tid < H) {
     const float l = s_l[tid];
-    a.lse[(int64_t)r * H + tid] =
+    a.lse[(int64_t)r * HT + h0 + tid] =
         l > 0.f ? (s_m[tid] + log2f(l)) * 0.6931471805599453f : -INFINITY;
   }
 }
@@ -528,14 +587,22 @@ AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t 
   return p;
 }
 
-hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, hipStream_t stream) {
+hipError_t launch_attention(const AttnArgs &args, int32_t n_heads, int32_t n_rows, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  dim3 grid((unsigned)(n_rows * a.n_split));
-  switch (n_heads) {
-    case 16: attn_kernel<1><<<grid, kAttnThreads, 0, stream>>>(a); break;
-    case 32: attn_kernel<2><<<grid, kAttnThreads, 0, stream>>>(a); break;
-    default: attn_kernel<4><<<grid, kAttnThreads, 0, stream>>>(a); break;
-  }
+  // 16 heads per work-group for 16-head layers, else 32 (64 heads: two head
+  // groups, so a work-group's registers and LDS leave room for a second one
+  // on its CU)
+  AttnArgs a = args;
+  a.n_heads = n_heads;
+  a.n_hgroups = n_heads == 64 ? 2 : 1;
+  a.n_rows = n_rows;
+  const int64_t rs = (int64_t)n_rows * a.n_split;
+  const int64_t blocks = a.n_hgroups == 1 ? rs : ((rs + 7) / 8) * 8 * a.n_hgroups;
+  dim3 grid((unsigned)blocks);
+  if (n_heads == 16)
+    attn_kernel<1><<<grid, kAttnThreads, 0, stream>>>(a);
+  else
+    attn_kernel<2><<<grid, kAttnThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split <= 1) return e;
   attn_merge_kernel<<<dim3((unsigned)(n_rows * n_heads / 2)), 256, 0, stream>>>(a, n_heads);

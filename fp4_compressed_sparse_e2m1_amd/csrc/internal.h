@@ -95,6 +95,11 @@ struct AttnArgs {
   int32_t tiles_per_split;    // key tiles (32 keys; 16-key blocks for 16 heads) per work-group
   float *part_o;              // [R][n_split][H][512]
   float *part_ml;             // [R][n_split][H][2]  (running max in log2 units, sum)
+  // set by launch_attention: all heads, head groups per row (a work-group
+  // takes one group of 16 or 32 heads), rows
+  int32_t n_heads;
+  int32_t n_hgroups;
+  int32_t n_rows;
 };
 
 // Key tiles per attention work-group step.
