@@ -37,13 +37,371 @@ namespace csa2 {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kTileKeys = kAttnTileKeys;
 constexpr int kMergeSplitLimit = 64;     // splits the merge kernel accepts
+constexpr float kLazyRescale = 8.0f;   // log2 units
+
+// Raw share of one key for lane (G, c) of wave w: the key at tile slot
+// 16w + c, channels [128G, 128G + 128) -- 64 bytes of E2M1 codes and the 8
+// scale bytes of those channels, or 128 E4M3 bytes of an SWA row.
+struct KeyFp4 {
+  uint4 a[4];
+  uint2 sc;
+  bool valid;
+};
+struct KeySwa {
+  uint4 a[8];
+  bool valid;
+};
+
+// Sparse attention, one work-group (4 waves) per (query row, split of its
+// keys, group of 16 heads).  Keys arrive in tiles of 64; wave w owns the tile's
+// keys 16w .. 16w + 15 with all 512 channels.
+//   * Lane (G, c) gathers channels [128G, 128G + 128) of key 16w + c and
+//     dequantises them to f16 (exact).
+//   * Logits: S^T = K Q^T by 16x16x32 MFMAs over the 512 channels (four
+//     independent chains of four); lane (G, c) ends with the logits of keys
+//     4G .. 4G + 3 for head c, so a head's maximum over the wave's keys takes
+//     three in-lane steps and two lane swaps.  Only the per-head maxima of the
+//     four waves cross between waves.
+//   * Online softmax in base 2, the running max raised only when a tile
+//     exceeds it by more than 2^8 (the O rescale is skipped, by wave ballot,
+//     otherwise).  Probabilities enter P.V in f16 and the normaliser sums the
+//     same rounded values.
+//   * P.V: the waves' P rows and dequantised keys go to LDS; wave w then
+//     accumulates O[:, 128w .. 128w + 127] over all 64 keys of the tile, the V
+//     operand read back with the hardware transposed LDS read.
+// Two work-group barriers per 64 keys.  A 32- or 64-head layer runs 2 or 4
+// head groups per row, given block ids that put them on one XCD, so the keys
+// they all gather come from its L2.
+constexpr int kKsHeads = 16;
+constexpr int kKsVStride = 512 + 8;    // halves per LDS key row (16-B writes of 16 rows on distinct banks)
+constexpr int kKsPStride = 64 + 8;     // halves per LDS P row
+
+__global__ void __launch_bounds__(kAttnThreads)
+attn_kernel(AttnArgs a) {
+  constexpr int H = kKsHeads;
+  __shared__ __attribute__((aligned(16))) _Float16 s_v[kAttnTileKeys * kKsVStride];
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[H * kKsPStride];
+  __shared__ __attribute__((aligned(16))) float s_wmax[H][4];
+  __shared__ __attribute__((aligned(16))) float s_alpha[H];
+  __shared__ float s_wl[4][H];
+  __shared__ float s_m[H], s_l[H];
+
+  // Work-group -> (row, split, head group): the head groups of one (row,
+  // split) get block ids equal modulo 8, so they run on one XCD (work-groups
+  // go to the 8 XCDs in turn); the grid is padded to whole sets of 8.
+  const int HT = a.n_heads;
+  int rs = blockIdx.x, hg = 0;
+  if (a.n_hgroups > 1) {
+    const int per = 8 * a.n_hgroups;
+    const int blk = blockIdx.x / per;
+    const int rem = blockIdx.x - blk * per;
+    hg = rem >> 3;
+    rs = blk * 8 + (rem & 7);
+  }
+  if (rs >= a.n_rows * a.n_split) return;
+  const int h0 = hg * H;
+  const int r = rs / a.n_split;
+  const int sp = rs - r * a.n_split;
+  const bool split = a.n_split > 1;
+  const bool merge_in = a.merge_in && !split;   // with a split the merge kernel folds (o, lse) in
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int G = lane >> 4;
+  const int c = lane & 15;
+
+  // the per-row scalars are read together (none waits on another)
+  int seq = a.row_seq[r];
+  int n_g = a.topk ? a.n_topk[r] : 0;
+  int64_t end = a.swa_kv ? a.swa_end[r] : 0;
+  const bool seq_ok = seq >= 0 && seq < a.n_seq;
+  if (!seq_ok) seq = 0;
+  n_g = (!seq_ok || n_g < 0) ? 0 : (n_g > a.k_pos ? a.k_pos : n_g);
+  int64_t s0 = 0;
+  int n_s = 0;
+  if (a.swa_kv && seq_ok) {
+    end = end < 0 ? 0 : (end > a.swa_len ? a.swa_len : end);
+    s0 = end - a.swa_window;
+    s0 = s0 < 0 ? 0 : s0;
+    n_s = (int)(end - s0);
+  }
+  constexpr int TK = kAttnTileKeys;
+  const int n_gt = (n_g + TK - 1) / TK;
+  const int n_all = n_gt + (n_s + TK - 1) / TK;
+  // this work-group's tiles: [t_begin, t_end)
+  const int t_begin = split ? sp * a.tiles_per_split : 0;
+  int t_end = split ? t_begin + a.tiles_per_split : n_all;
+  t_end = t_end < n_all ? t_end : n_all;
+
+  // Q operand: qa[t] = q[r][h0 + c][128G + 8t .. +7] in f16, t < 16 (the
+  // contraction over the 512 channels runs in this lane-consistent order)
+  f16x8 qa[16];
+  {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * HT + h0 + c) * 512 + 128 * G);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) qa[t] = bf16x8_to_f16(qp[t]);
+  }
+
+  // O[:, 128w + 16db + c] for heads 4G .. 4G + 3 (lane (G, c), element i)
+  f32x4 acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (merge_in) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = h0 + 4 * G + i;
+      const float lin = a.lse[(int64_t)r * HT + h];
+      if (lin != -INFINITY) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[db][i] = a.o[((int64_t)r * HT + h) * 512 + 128 * w + 16 * db + c];
+      }
+    }
+  }
+  // softmax state of head c, in every lane (G, c) of every wave: the running
+  // max (log2 units), and the normaliser as per-lane partial sums reduced at
+  // the end
+  float m_run = -INFINITY, l_thr = 0.f;
+  if (merge_in) {
+    const float lin = a.lse[(int64_t)r * HT + h0 + c];
+    if (lin != -INFINITY) {
+      m_run = lin * 1.4426950408889634f;
+      l_thr = (w == 0 && G == 0) ? 1.f : 0.f;
+    }
+  }
+
+  const uint8_t *kv_codes = a.kv_codes + (int64_t)seq * a.cap * 256;
+  const uint8_t *kv_scales = a.kv_scales + (int64_t)seq * a.cap * 32;
+  const uint8_t *swa = a.swa_kv ? a.swa_kv + ((int64_t)seq * a.swa_len) * 512 : nullptr;
+  const int32_t *topk = a.topk ? a.topk + (int64_t)r * a.k_pos : nullptr;
+
+  // The entry id of this lane's key in tile T, read ahead of need and without
+  // waiting for n_topk (every slot below k_pos is inside the row).
+  auto load_id = [&](int T) -> int32_t {
+    const int slot = T * TK + 16 * w + c;
+    return (topk && slot < a.k_pos) ? topk[slot] : -1;
+  };
+  auto load_fp4 = [&](int T, int32_t id) {
+    KeyFp4 k;
+    const int slot = T * TK + 16 * w + c;
+    const int64_t e = slot < n_g ? id : -1;
+    k.valid = e >= 0 && e < a.cap;
+    const int64_t el = k.valid ? e : 0;
+    const uint4 *cp = reinterpret_cast<const uint4 *>(kv_codes + el * 256 + 64 * G);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k.a[j] = cp[j];
+    k.sc = *reinterpret_cast<const uint2 *>(kv_scales + el * 32 + 8 * G);
+    return k;
+  };
+  auto load_swa = [&](int Ts) {       // tile index within the SWA rows
+    KeySwa k;
+    const int slot = Ts * TK + 16 * w + c;
+    k.valid = slot < n_s;
+    const int64_t row = k.valid ? s0 + slot : 0;
+    const uint4 *p = reinterpret_cast<const uint4 *>(swa + row * 512 + 128 * G);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k.a[j] = p[j];
+    return k;
+  };
+  // dequantise to kf[t] = channels 128G + 8t .. +7 (skipped keys load entry 0
+  // and are zeroed, so no stale byte pattern can reach the P.V product)
+  f16x8 kf[16];
+  auto dequant_fp4 = [&](const KeyFp4 &k) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t sw = (t < 8 ? k.sc.x : k.sc.y) >> (8 * ((t >> 1) & 3));
+      const _Float16 sc = e4m3_to_f16(sw & 0xFFu);
+      const uint32_t dw = t % 4 == 0 ? k.a[t / 4].x : t % 4 == 1 ? k.a[t / 4].y : t % 4 == 2 ? k.a[t / 4].z : k.a[t / 4].w;
+      kf[t] = e2m1x8_to_f16(dw) * f16x8{sc, sc, sc, sc, sc, sc, sc, sc};
+      if (!k.valid) kf[t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  };
+  auto dequant_swa = [&](const KeySwa &k) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint4 v = k.a[t / 2];
+      kf[t] = (t % 2 == 0) ? e4m3x8_to_f16(v.x, v.y) : e4m3x8_to_f16(v.z, v.w);
+      if (!k.valid) kf[t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  };
+
+  // One tile (the dequantised keys in kf): logits, online softmax, P.V.
+  auto compute = [&](bool valid) {
+    // the wave's valid keys (lanes 0..15 hold keys 0..15)
+    const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(valid) & 0xFFFFu;
+    f32x4 q0 = {0.f, 0.f, 0.f, 0.f}, q1 = q0, q2 = q0, q3 = q0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      q0 = mfma16x16x32(kf[t], qa[t], q0);
+      q1 = mfma16x16x32(kf[4 + t], qa[4 + t], q1);
+      q2 = mfma16x16x32(kf[8 + t], qa[8 + t], q2);
+      q3 = mfma16x16x32(kf[12 + t], qa[12 + t], q3);
+    }
+    // lane (G, c): logits of keys 4G + i for head c
+    float sv[4];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = (q0[i] + q1[i]) + (q2[i] + q3[i]);
+      sv[i] = ((vmask >> (4 * G + i)) & 1u) ? x * a.scale_log2 : -INFINITY;
+      lmax = fmaxf(lmax, sv[i]);
+    }
+    lmax = fmaxf(lmax, swap_rows16(lmax));                       // lanes c, c + 16
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(lmax), __float_as_int(lmax), false, false);
+      lmax = fmaxf(lmax, __int_as_float(lane < 32 ? sw[1] : sw[0]));   // and c + 32, c + 48
+    }
+    if (G == 0) s_wmax[c][w] = lmax;
+    __syncthreads();
+    const float4 wm = *reinterpret_cast<const float4 *>(&s_wmax[c][0]);
+    const float tmax = fmaxf(fmaxf(wm.x, wm.y), fmaxf(wm.z, wm.w));
+    float m_new = m_run;
+    if (m_run == -INFINITY || tmax > m_run + kLazyRescale) m_new = fmaxf(tmax, m_run);
+    // the hardware exp2 (no denormal-range fix-up): arguments are <= 2^8, and
+    // results below 2^-126 are negligible weights (f16 drops them too)
+    const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    _Float16 ph[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_new);
+      ph[i] = (_Float16)p;
+      psum += (float)ph[i];
+    }
+    l_thr = l_thr * alpha + psum;
+    m_run = m_new;
+    if (w == 0 && G == 0) s_alpha[c] = alpha;
+    // this wave's keys (all channels) and P values to LDS
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      *reinterpret_cast<f16x8 *>(&s_v[(16 * w + c) * kKsVStride + 128 * G + 8 * t]) = kf[t];
+    *reinterpret_cast<f16x4 *>(&s_p[c * kKsPStride + 16 * w + 4 * G]) = f16x4{ph[0], ph[1], ph[2], ph[3]};
+    __syncthreads();
+    // O[:, quarter w] = alpha * O + P V over the tile's 64 keys (the rescale
+    // is skipped while the running maxima of these heads stand still)
+    const float4 al = *reinterpret_cast<const float4 *>(&s_alpha[4 * G]);
+    if (__builtin_amdgcn_ballot_w64(al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        acc[db][0] *= al.x;
+        acc[db][1] *= al.y;
+        acc[db][2] *= al.z;
+        acc[db][3] *= al.w;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // A: P[head c][keys 32kk + 8G .. +7]; B: V[keys 32kk + 8G .. +7][channel
+      // 128w + 16db + c], from rows 32kk + 8G + 4h + c/4 (h = 0, 1) read
+      // transposed
+      const f16x8 pa = *reinterpret_cast<const f16x8 *>(&s_p[c * kKsPStride + 32 * kk + 8 * G]);
+      const _Float16 *r0 = &s_v[(32 * kk + 8 * G + (c >> 2)) * kKsVStride + 128 * w + 4 * (c & 3)];
+      const _Float16 *r1 = r0 + 4 * kKsVStride;
+#pragma unroll
+      for (int db = 0; db < 8; db += 2) {
+        f16x8 vb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f16x4 lo = lds_read_tr16(r0 + 16 * (db + u));
+          const f16x4 hi = lds_read_tr16(r1 + 16 * (db + u));
+          vb[u] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[db + u] = mfma16x16x32(pa, vb[u], acc[db + u]);
+      }
+    }
+    // (the next tile writes LDS only after its first barrier, which every
+    // wave reaches after finishing these reads)
+  };
+
+  // Top-K tiles: while a tile is computed the next two are in flight (the
+  // gathers are random HBM reads); the tile registers rotate by copy.
+  const int g_end = t_end < n_gt ? t_end : n_gt;
+  {
+    int32_t id2 = load_id(t_begin + 2);
+    KeyFp4 ka, kb;
+    if (t_begin < g_end) ka = load_fp4(t_begin, load_id(t_begin));
+    if (t_begin + 1 < g_end) kb = load_fp4(t_begin + 1, load_id(t_begin + 1));
+    for (int T = t_begin; T < g_end; ++T) {
+      dequant_fp4(ka);
+      const bool v = ka.valid;
+      ka = kb;
+      if (T + 2 < g_end) kb = load_fp4(T + 2, id2);
+      id2 = load_id(T + 3);
+      compute(v);
+    }
+  }
+  // SWA tiles (consecutive rows), the next one in flight
+  {
+    const int sw_begin = (t_begin > n_gt ? t_begin : n_gt) - n_gt;
+    const int sw_end = t_end - n_gt;
+    KeySwa ks;
+    if (sw_begin < sw_end) ks = load_swa(sw_begin);
+    for (int Ts = sw_begin; Ts < sw_end; ++Ts) {
+      dequant_swa(ks);
+      const bool v = ks.valid;
+      if (Ts + 1 < sw_end) ks = load_swa(Ts + 1);
+      compute(v);
+    }
+  }
+
+  // normaliser of head c: the lanes of head c, then the waves
+  {
+    float l = l_thr + swap_rows16(l_thr);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l), __float_as_int(l), false, false);
+    l += __int_as_float(lane < 32 ? sw[1] : sw[0]);
+    if (G == 0) s_wl[w][c] = l;
+  }
+  __syncthreads();
+  if (tid < H) {
+    s_m[tid] = m_run;                   // lane tid holds head tid's state
+    s_l[tid] = (s_wl[0][tid] + s_wl[1][tid]) + (s_wl[2][tid] + s_wl[3][tid]);
+  }
+  __syncthreads();
+  if (split) {
+    // unnormalised partial: O, running max (log2 units) and sum per head
+    const int64_t part = (int64_t)r * a.n_split + sp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * G + i;
+      float *prow = a.part_o + (part * HT + h0 + h) * 512 + 128 * w + c;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) prow[16 * db] = acc[db][i];
+    }
+    if (tid < H) {
+      a.part_ml[(part * HT + h0 + tid) * 2] = s_m[tid];
+      a.part_ml[(part * HT + h0 + tid) * 2 + 1] = s_l[tid];
+    }
+    return;
+  }
+  // normalise and store
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * G + i;
+    const float l = s_l[h];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float *orow = a.o + ((int64_t)r * HT + h0 + h) * 512 + 128 * w + c;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) orow[16 * db] = acc[db][i] * inv;
+  }
+  if (tid < H) {
+    const float l = s_l[tid];
+    a.lse[(int64_t)r * HT + h0 + tid] = l > 0.f ? (s_m[tid] + log2f(l)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------
+// Channel-quarter variant, used for 64-head layers (two 32-head work-groups
+// per row): keys in tiles of 32, wave w owns the channel quarter
+// [128w, 128w + 128) of every key -- it dequantises only that quarter, so a
+// key is dequantised once for 32 heads -- and the four partial logits are
+// summed through LDS ([head][key] rows).  For 16- and 32-head groups the
+// key-split kernel above moves less data through LDS.
+constexpr int kCqTileKeys = 32;
 constexpr int kVnStride = 128 + 8;     // halves per LDS key row: a wave's 128 channels + pad
                                        // (16-B writes of 16 rows land on distinct banks)
 constexpr int kPStride = 40;           // halves per P row
 constexpr int kSPStride = 32 + 4;      // floats per partial-logit row (one head, 32 keys + pad)
-constexpr float kLazyRescale = 8.0f;   // log2 units
 
 // One wave's raw share of a 32-key tile (two 16-key blocks kb): FP4 codes of
 // its channel quarter plus two scale bytes per key, or 32 E4M3 bytes per key
@@ -80,21 +438,21 @@ __device__ __forceinline__ float group_sum(float x) {
 
 template <int HB>
 __global__ void __launch_bounds__(kAttnThreads)
-attn_kernel(AttnArgs a) {
+attn_cq_kernel(AttnArgs a) {
   static_assert(HB == 1 || HB == 2, "a work-group takes 16 or 32 heads");
   constexpr int H = 16 * HB;
   constexpr int TPH = kAttnThreads / H;        // softmax threads per head
-  constexpr int KPT = kTileKeys / TPH;         // keys per softmax thread
+  constexpr int KPT = kCqTileKeys / TPH;         // keys per softmax thread
 
   // partial logits, [wave][head][key]: the MFMA result goes out as single
   // words with consecutive keys in consecutive banks, and each softmax thread
   // reads its keys of one head contiguously
   __shared__ __attribute__((aligned(16))) float s_part[4][H][kSPStride];
-  __shared__ __attribute__((aligned(16))) _Float16 s_vn[4][kTileKeys * kVnStride];
+  __shared__ __attribute__((aligned(16))) _Float16 s_vn[4][kCqTileKeys * kVnStride];
   __shared__ __attribute__((aligned(16))) _Float16 s_p[H * kPStride];
   __shared__ __attribute__((aligned(16))) float s_alpha[H];
   __shared__ float s_m[H], s_l[H];
-  __shared__ int s_valid[kTileKeys];
+  __shared__ int s_valid[kCqTileKeys];
 
   // Work-group -> (row, split, head group).  With several head groups, the
   // groups of one (row, split) get block ids equal modulo 8, so they run on
@@ -136,8 +494,8 @@ attn_kernel(AttnArgs a) {
     s0 = s0 < 0 ? 0 : s0;
     n_s = (int)(end - s0);
   }
-  const int n_gt = (n_g + kTileKeys - 1) / kTileKeys;
-  const int n_all = n_gt + (n_s + kTileKeys - 1) / kTileKeys;
+  const int n_gt = (n_g + kCqTileKeys - 1) / kCqTileKeys;
+  const int n_all = n_gt + (n_s + kCqTileKeys - 1) / kCqTileKeys;
   // this work-group's tiles: [t_begin, t_end)
   const int t_begin = split ? sp * a.tiles_per_split : 0;
   int t_end = split ? t_begin + a.tiles_per_split : n_all;
@@ -198,7 +556,7 @@ attn_kernel(AttnArgs a) {
   auto load_ids = [&](int tile, int32_t (&e)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int slot = tile * kTileKeys + 16 * kb + c;
+      const int slot = tile * kCqTileKeys + 16 * kb + c;
       e[kb] = (topk && slot < a.k_pos) ? topk[slot] : -1;
     }
   };
@@ -206,7 +564,7 @@ attn_kernel(AttnArgs a) {
     Fp4Tile t;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int slot = tile * kTileKeys + 16 * kb + c;
+      const int slot = tile * kCqTileKeys + 16 * kb + c;
       const int64_t e = slot < n_g ? ids[kb] : -1;
       const bool ok = e >= 0 && e < a.cap;
       t.valid[kb] = ok;
@@ -220,7 +578,7 @@ attn_kernel(AttnArgs a) {
     SwaTile t;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int slot = tile * kTileKeys + 16 * kb + c;
+      const int slot = tile * kCqTileKeys + 16 * kb + c;
       const bool ok = slot < n_s;
       t.valid[kb] = ok;
       const int64_t row = ok ? s0 + slot : 0;
@@ -566,8 +924,9 @@ attn_merge_kernel(AttnArgs a, int H) {
 hipError_t prepare_attention() { return hipSuccess; }
 
 AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t window) {
-  (void)n_heads;
-  const int max_tiles = (k_pos + kTileKeys - 1) / kTileKeys + (window + kTileKeys - 1) / kTileKeys;
+  // keys per tile of the kernel that serves this head count
+  const int tk = n_heads == 64 ? kCqTileKeys : kAttnTileKeys;
+  const int max_tiles = (k_pos + tk - 1) / tk + (window + tk - 1) / tk;
   AttnPlan p = {1, max_tiles > 0 ? max_tiles : 1, 0};
   // Few rows leave most of the 256 CUs idle: spread each row's key tiles over
   // several work-groups (about 256 in all; one tile each when that many
@@ -589,20 +948,18 @@ AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t 
 
 hipError_t launch_attention(const AttnArgs &args, int32_t n_heads, int32_t n_rows, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  // 16 heads per work-group for 16-head layers, else 32 (64 heads: two head
-  // groups, so a work-group's registers and LDS leave room for a second one
-  // on its CU)
+  // 16- and 32-head layers: the key-split kernel, 16 heads per work-group;
+  // 64-head layers: the channel-quarter kernel, 32 heads per work-group
   AttnArgs a = args;
   a.n_heads = n_heads;
-  a.n_hgroups = n_heads == 64 ? 2 : 1;
+  a.n_hgroups = n_heads == 64 ? 2 : n_heads / kKsHeads;
   a.n_rows = n_rows;
   const int64_t rs = (int64_t)n_rows * a.n_split;
   const int64_t blocks = a.n_hgroups == 1 ? rs : ((rs + 7) / 8) * 8 * a.n_hgroups;
-  dim3 grid((unsigned)blocks);
-  if (n_heads == 16)
-    attn_kernel<1><<<grid, kAttnThreads, 0, stream>>>(a);
+  if (n_heads == 64)
+    attn_cq_kernel<2><<<dim3((unsigned)blocks), kAttnThreads, 0, stream>>>(a);
   else
-    attn_kernel<2><<<grid, kAttnThreads, 0, stream>>>(a);
+    attn_kernel<<<dim3((unsigned)blocks), kAttnThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split <= 1) return e;
   attn_merge_kernel<<<dim3((unsigned)(n_rows * n_heads / 2)), 256, 0, stream>>>(a, n_heads);

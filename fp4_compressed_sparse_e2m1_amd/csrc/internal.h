@@ -103,7 +103,7 @@ struct AttnArgs {
 };
 
 // Key tiles per attention work-group step.
-constexpr int kAttnTileKeys = 32;
+constexpr int kAttnTileKeys = 64;
 
 // Work-group split of the attention rows: n_split partial results per row
 // (1 = no split, no workspace).
