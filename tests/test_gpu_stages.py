@@ -386,6 +386,17 @@ def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
     refs = [oracle_attn(c, r) for r in range(n_rows)]
     check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o"] for x in refs]),
                     np.stack([x["lse"] for x in refs]), f"H{H} k{k_pos} w{window}")
+    # the same result as global attention followed by the SWA merge
+    ws_g = csa2.attn_workspace(n_rows, H, k_pos, 0) if split else None
+    ws_m = csa2.attn_workspace(n_rows, H, 0, window) if split else None
+    o2 = torch.empty_like(o)
+    lse2 = torch.empty_like(lse)
+    csa2.csa2_sparse_attn(c["cache"], dev(c["q"]), dev(c["row_seq"]), dev(c["topk"]), dev(c["ntopk"]),
+                          SCALE, o2, lse2, workspace=ws_g)
+    csa2.csa2_swa_merge(dev(c["q"]), dev(c["row_seq"]), swa, SCALE, o2, lse2, workspace=ws_m)
+    torch.cuda.synchronize()
+    check_attention(o2.cpu().numpy(), lse2.cpu().numpy(), np.stack([x["o"] for x in refs]),
+                    np.stack([x["lse"] for x in refs]), f"H{H} k{k_pos} w{window} merged")
 
 
 @pytest.mark.parametrize("split", [False, True])
