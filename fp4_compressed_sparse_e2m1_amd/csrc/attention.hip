@@ -949,18 +949,20 @@ AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t 
 hipError_t launch_attention(const AttnArgs &args, int32_t n_heads, int32_t n_rows, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   // 16- and 32-head layers: the key-split kernel, 16 heads per work-group;
-  // 64-head layers: the channel-quarter kernel, 32 heads per work-group
+  // 64-head layers: the 64-head kernel, one work-group per row (or split)
   AttnArgs a = args;
   a.n_heads = n_heads;
-  a.n_hgroups = n_heads == 64 ? 2 : n_heads / kKsHeads;
+  a.n_hgroups = n_heads == 64 ? 1 : n_heads / kKsHeads;
   a.n_rows = n_rows;
   const int64_t rs = (int64_t)n_rows * a.n_split;
   const int64_t blocks = a.n_hgroups == 1 ? rs : ((rs + 7) / 8) * 8 * a.n_hgroups;
-  if (n_heads == 64)
-    attn_cq_kernel<2><<<dim3((unsigned)blocks), kAttnThreads, 0, stream>>>(a);
-  else
+  hipError_t e;
+  if (n_heads == 64) {
+    e = launch_attention_h64(a, blocks, stream);
+  } else {
     attn_kernel<<<dim3((unsigned)blocks), kAttnThreads, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || a.n_split <= 1) return e;
   attn_merge_kernel<<<dim3((unsigned)(n_rows * n_heads / 2)), 256, 0, stream>>>(a, n_heads);
   return hipGetLastError();

@@ -115,6 +115,10 @@ struct AttnPlan {
 AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t window);
 
 hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, hipStream_t stream);
+// The 64-head kernel alone (one work-group per row or split of a row; the
+// caller sets n_heads = 64, n_hgroups = 1 and n_rows).  Built in its own
+// translation unit: its O accumulators stay in the matrix-core registers.
+hipError_t launch_attention_h64(const AttnArgs &a, int64_t blocks, hipStream_t stream);
 hipError_t prepare_attention();
 
 // ---------------------------------------------------------------- quantise
