@@ -23,9 +23,9 @@
 //         running max is raised only when a tile exceeds it by more than 2^8,
 //         so most tiles leave O alone; P enters P.V in f16 and the normaliser
 //         sums the same rounded values.
-//   C(t): O^T[quarter q][heads 32 h2 .. 32 h2 + 31] = alpha * O^T + V^T P^T
+//   C(t): O^T[channels 64w .. 64w + 63][all heads] = alpha * O^T + V^T P^T
 //         over the tile's 32 keys, the V operand read back from LDS with the
-//         hardware transposed read.
+//         hardware transposed read (each eighth of the channels read once).
 // The stages are software-pipelined, two work-group barriers per tile:
 //     [C(t-1) + B(t)]  barrier  [A(t+1)]  barrier
 // and each wave's raw gathers are issued three tiles ahead of their use.
@@ -73,8 +73,8 @@ attn_h64_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int q = w & 3;           // channel quarter (A, C)
-  const int h2 = w >> 2;         // key block (A), head half (C)
+  const int q = w & 3;           // channel quarter (A)
+  const int h2 = w >> 2;         // key block (A)
   const int G = lane >> 4;
   const int c = lane & 15;
   const int hs = 8 * w + (lane & 7);    // softmax head (B)
@@ -213,20 +213,20 @@ attn_h64_kernel(AttnArgs a) {
   }
 
   // O^T accumulators: acc[hb][db] lane (G, c) holds
-  // O[32h2 + 16hb + c][128q + 16db + 4G + i]
-  f32x4 acc[2][8];
+  // O[16hb + c][64w + 16db + 4G + i]
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
+  for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 4; ++db) acc[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (merge_in) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int64_t h = (int64_t)r * H + 32 * h2 + 16 * hb + c;
+    for (int hb = 0; hb < 4; ++hb) {
+      const int64_t h = (int64_t)r * H + 16 * hb + c;
       if (a.lse[h] != -INFINITY) {
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-          acc[hb][db] = *reinterpret_cast<const f32x4 *>(a.o + h * 512 + 128 * q + 16 * db + 4 * G);
+        for (int db = 0; db < 4; ++db)
+          acc[hb][db] = *reinterpret_cast<const f32x4 *>(a.o + h * 512 + 64 * w + 16 * db + 4 * G);
       }
     }
   }
@@ -320,36 +320,36 @@ attn_h64_kernel(AttnArgs a) {
     s_alpha[T & 1][hs] = alpha;          // the eight lanes of the head write the same value
   };
 
-  // ---- C(T): O^T[quarter q][head half h2] = alpha * O^T + V^T P^T over the
-  // tile's 32 keys.  The rescale (rare) comes first, on its own.
+  // ---- C(T): O^T[channels 64w .. 64w + 63][all heads] = alpha * O^T + V^T P^T
+  // over the tile's 32 keys.  The rescale (rare) comes first, on its own.
   auto rescale = [&](int T) {
-    const float al0 = s_alpha[T & 1][32 * h2 + c];
-    const float al1 = s_alpha[T & 1][32 * h2 + 16 + c];
-    if (__builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f)) {
+    float al[4];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        acc[0][db] *= al0;
-        acc[1][db] *= al1;
-      }
+    for (int hb = 0; hb < 4; ++hb) al[hb] = s_alpha[T & 1][16 * hb + c];
+    if (__builtin_amdgcn_ballot_w64(al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f)) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[hb][db] *= al[hb];
     }
   };
   auto stage_c = [&](int T) {
-    // B operand: P^T[keys 8G .. 8G + 7][head 32h2 + 16hb + c]
-    f16x8 pb[2];
+    // B operand: P^T[keys 8G .. 8G + 7][head 16hb + c]
+    f16x8 pb[4];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-      pb[hb] = *reinterpret_cast<const f16x8 *>(&s_p[T & 1][(32 * h2 + 16 * hb + c) * kPS + 8 * G]);
-    // A operand of channel block db: V^T[channel 16db + c][keys 8G .. 8G + 7],
-    // read transposed from rows 8G + 4h + c/4 (h = 0, 1), channels 16db + 4 (c % 4)
-    const _Float16 *r0 = &s_vn[T & 1][q][(8 * G + (c >> 2)) * kVS + 4 * (c & 3)];
+    for (int hb = 0; hb < 4; ++hb) pb[hb] = *reinterpret_cast<const f16x8 *>(&s_p[T & 1][(16 * hb + c) * kPS + 8 * G]);
+    // A operand of channel block db: V^T[channel 64w + 16db + c][keys 8G .. 8G + 7],
+    // read transposed from rows 8G + 4h + c/4 (h = 0, 1) of quarter w / 2,
+    // channels 64 (w % 2) + 16db + 4 (c % 4)
+    const _Float16 *r0 = &s_vn[T & 1][w >> 1][(8 * G + (c >> 2)) * kVS + 64 * (w & 1) + 4 * (c & 3)];
     const _Float16 *r1 = r0 + 4 * kVS;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < 4; ++db) {
       const f16x4 lo = lds_read_tr16(r0 + 16 * db);
       const f16x4 hi = lds_read_tr16(r1 + 16 * db);
       const f16x8 va = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) acc[hb][db] = mfma16x16x32(va, pb[hb], acc[hb][db]);
+      for (int hb = 0; hb < 4; ++hb) acc[hb][db] = mfma16x16x32(va, pb[hb], acc[hb][db]);
     }
   };
 
@@ -418,10 +418,10 @@ attn_h64_kernel(AttnArgs a) {
     // unnormalised partial: O, running max (log2 units) and sum per head
     const int64_t part = (int64_t)r * a.n_split + sp;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float *prow = a.part_o + (part * H + 32 * h2 + 16 * hb + c) * 512 + 128 * q + 4 * G;
+    for (int hb = 0; hb < 4; ++hb) {
+      float *prow = a.part_o + (part * H + 16 * hb + c) * 512 + 64 * w + 4 * G;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(prow + 16 * db) = acc[hb][db];
+      for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4 *>(prow + 16 * db) = acc[hb][db];
     }
     if (tid < H) {
       a.part_ml[(part * H + tid) * 2] = s_m[tid];
@@ -431,13 +431,13 @@ attn_h64_kernel(AttnArgs a) {
   }
   // normalise and store
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int h = 32 * h2 + 16 * hb + c;
+  for (int hb = 0; hb < 4; ++hb) {
+    const int h = 16 * hb + c;
     const float l = s_l[h];
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float *orow = a.o + ((int64_t)r * H + h) * 512 + 128 * q + 4 * G;
+    float *orow = a.o + ((int64_t)r * H + h) * 512 + 64 * w + 4 * G;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(orow + 16 * db) = acc[hb][db] * inv;
+    for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4 *>(orow + 16 * db) = acc[hb][db] * inv;
   }
   if (tid < H) {
     const float l = s_l[tid];
