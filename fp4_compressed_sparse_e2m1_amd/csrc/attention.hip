@@ -8,27 +8,12 @@
 // The latent is shared by all heads and is both key and value (one latent per
 // entry, no separate V in the 356-B entry).
 //
-// One work-group (4 waves) handles one query row (or one split of its keys)
-// and a group of 16 heads (16-head layers) or 32 heads (32- and 64-head
-// layers; a 64-head row takes two work-groups, given block ids that place
-// both on one XCD so the gathered keys come from its L2 once).  Keys are
-// consumed in tiles of 32 (two blocks of 16): the Top-K tiles first, with the
-// ids read and the gathers issued two tiles ahead, then the SWA tiles.  Wave w
-// owns the channel quarter [128w, 128w+128):
-//   * it gathers only its quarter of each key (16 B of E2M1 codes + 2 scale
-//     bytes, or 32 B of E4M3 for SWA rows) and dequantises it once, exactly,
-//     to f16;
-//   * Q.K^T: it computes the partial logits over its quarter with 16x16x32
-//     MFMAs (rows = 16 heads, columns = 16 keys); the four partials are summed
-//     through LDS ([head][key] rows, so the writes and the softmax reads are
-//     free of bank conflicts);
-//   * P.V: it keeps its dequantised quarter in LDS (natural layout) and
-//     accumulates O[:, quarter] with MFMAs (rows = 16 heads, columns = 16
-//     channels, contraction = the 32 keys of the tile), reading the V
-//     operand back with the hardware transposed LDS read.
-// The softmax is the online (running max) form in base 2; the running max is
-// only raised when a tile's maximum exceeds it by more than 2^8, so most tiles
-// skip the rescale of O.  Probabilities enter the P.V product in f16 and the
+// This file holds the 16- and 32-head kernel (keys split between the waves of
+// a work-group, described below), the merge of split rows and the launch
+// plan; 64-head layers run the kernel in attention64.hip.  Both use the
+// online (running max) softmax in base 2; the running max is only raised
+// when a tile's maximum exceeds it by more than 2^8, so most tiles skip the
+// rescale of O.  Probabilities enter the P.V product in f16 and the
 // normaliser sums the same rounded values, so the weights stay normalised.
 #include "device.h"
 #include "internal.h"
@@ -390,430 +375,6 @@ attn_kernel(AttnArgs a) {
   }
 }
 
-// ------------------------------------------------------------------
-// Channel-quarter variant, used for 64-head layers (two 32-head work-groups
-// per row): keys in tiles of 32, wave w owns the channel quarter
-// [128w, 128w + 128) of every key -- it dequantises only that quarter, so a
-// key is dequantised once for 32 heads -- and the four partial logits are
-// summed through LDS ([head][key] rows).  For 16- and 32-head groups the
-// key-split kernel above moves less data through LDS.
-constexpr int kCqTileKeys = 32;
-constexpr int kVnStride = 128 + 8;     // halves per LDS key row: a wave's 128 channels + pad
-                                       // (16-B writes of 16 rows land on distinct banks)
-constexpr int kPStride = 40;           // halves per P row
-constexpr int kSPStride = 32 + 4;      // floats per partial-logit row (one head, 32 keys + pad)
-
-// One wave's raw share of a 32-key tile (two 16-key blocks kb): FP4 codes of
-// its channel quarter plus two scale bytes per key, or 32 E4M3 bytes per key
-// of an SWA row.
-struct Fp4Tile {
-  uint4 a[2];
-  uint32_t sc[2];
-  bool valid[2];
-};
-struct SwaTile {
-  uint4 a[2];       // bytes 0..15 of the lane's 32
-  uint4 b[2];       // bytes 16..31
-  bool valid[2];
-};
-
-// Max / sum over each aligned group of N lanes (N = 2, 4, 8 or 16: a quad,
-// half row or row of the DPP network), in every lane of the group.
-template <int N>
-__device__ __forceinline__ float group_max(float x) {
-  if (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
-  if (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
-  if (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  if (N >= 16) x = fmaxf(x, dpp<kDppRowRor8>(x));
-  return x;
-}
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  if (N >= 2) x += dpp<kDppXor1>(x);
-  if (N >= 4) x += dpp<kDppXor2>(x);
-  if (N >= 8) x += dpp<kDppHalfMirror>(x);
-  if (N >= 16) x += dpp<kDppRowRor8>(x);
-  return x;
-}
-
-template <int HB>
-__global__ void __launch_bounds__(kAttnThreads)
-attn_cq_kernel(AttnArgs a) {
-  static_assert(HB == 1 || HB == 2, "a work-group takes 16 or 32 heads");
-  constexpr int H = 16 * HB;
-  constexpr int TPH = kAttnThreads / H;        // softmax threads per head
-  constexpr int KPT = kCqTileKeys / TPH;         // keys per softmax thread
-
-  // partial logits, [wave][head][key]: the MFMA result goes out as single
-  // words with consecutive keys in consecutive banks, and each softmax thread
-  // reads its keys of one head contiguously
-  __shared__ __attribute__((aligned(16))) float s_part[4][H][kSPStride];
-  __shared__ __attribute__((aligned(16))) _Float16 s_vn[4][kCqTileKeys * kVnStride];
-  __shared__ __attribute__((aligned(16))) _Float16 s_p[H * kPStride];
-  __shared__ __attribute__((aligned(16))) float s_alpha[H];
-  __shared__ float s_m[H], s_l[H];
-  __shared__ int s_valid[kCqTileKeys];
-
-  // Work-group -> (row, split, head group).  With several head groups, the
-  // groups of one (row, split) get block ids equal modulo 8, so they run on
-  // one XCD (work-groups go to the 8 XCDs in turn) and share its L2 for the
-  // gathered keys; the grid is padded to whole sets of 8.
-  const int HT = a.n_heads;
-  int rs = blockIdx.x, hg = 0;
-  if (a.n_hgroups > 1) {
-    const int per = 8 * a.n_hgroups;
-    const int blk = blockIdx.x / per;
-    const int rem = blockIdx.x - blk * per;
-    hg = rem >> 3;
-    rs = blk * 8 + (rem & 7);
-  }
-  if (rs >= a.n_rows * a.n_split) return;
-  const int h0 = hg * H;
-  const int r = rs / a.n_split;
-  const int sp = rs - r * a.n_split;
-  const bool split = a.n_split > 1;
-  const bool merge_in = a.merge_in && !split;   // with a split the merge kernel folds (o, lse) in
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int G = lane >> 4;
-  const int c = lane & 15;
-
-  // the per-row scalars are read together (none waits on another)
-  int seq = a.row_seq[r];
-  int n_g = a.topk ? a.n_topk[r] : 0;
-  int64_t end = a.swa_kv ? a.swa_end[r] : 0;
-  const bool seq_ok = seq >= 0 && seq < a.n_seq;
-  if (!seq_ok) seq = 0;
-  n_g = (!seq_ok || n_g < 0) ? 0 : (n_g > a.k_pos ? a.k_pos : n_g);
-  int64_t s0 = 0;
-  int n_s = 0;
-  if (a.swa_kv && seq_ok) {
-    end = end < 0 ? 0 : (end > a.swa_len ? a.swa_len : end);
-    s0 = end - a.swa_window;
-    s0 = s0 < 0 ? 0 : s0;
-    n_s = (int)(end - s0);
-  }
-  const int n_gt = (n_g + kCqTileKeys - 1) / kCqTileKeys;
-  const int n_all = n_gt + (n_s + kCqTileKeys - 1) / kCqTileKeys;
-  // this work-group's tiles: [t_begin, t_end)
-  const int t_begin = split ? sp * a.tiles_per_split : 0;
-  int t_end = split ? t_begin + a.tiles_per_split : n_all;
-  t_end = t_end < n_all ? t_end : n_all;
-
-  // Q operand: qa[hb][t] = q[r][h0 + 16hb + c][128w + 32G + 8t .. +7] in f16.
-  f16x8 qa[HB][4];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * HT + h0 + 16 * hb + c) * 512 +
-                                                      128 * w + 32 * G);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) qa[hb][t] = bf16x8_to_f16(qp[t]);
-  }
-
-  // Running state.  O[hb][db]: lane (G, c) holds heads 16hb + 4G + i (i < 4)
-  // at channel 128w + 16db + c.
-  f32x4 acc_o[HB][8];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-    for (int db = 0; db < 8; ++db) acc_o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (merge_in) {
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 16 * hb + 4 * G + i;
-        const float lin = a.lse[(int64_t)r * HT + h0 + h];
-        if (lin != -INFINITY) {
-#pragma unroll
-          for (int db = 0; db < 8; ++db)
-            acc_o[hb][db][i] = a.o[((int64_t)r * HT + h0 + h) * 512 + 128 * w + 16 * db + c];
-        }
-      }
-  }
-  // Softmax state of head tid / TPH, held by its TPH threads (consecutive
-  // lanes of one wave): the running max (log2 units) in every one of them,
-  // the normaliser as per-thread partial sums, reduced once at the end.
-  float m_run = -INFINITY, l_thr = 0.f;
-  if (merge_in) {
-    const float lin = a.lse[(int64_t)r * HT + h0 + tid / TPH];
-    if (lin != -INFINITY) {
-      m_run = lin * 1.4426950408889634f;
-      l_thr = (tid % TPH) == 0 ? 1.f : 0.f;
-    }
-  }
-
-  const uint8_t *kv_codes = a.kv_codes + (int64_t)seq * a.cap * 256;
-  const uint8_t *kv_scales = a.kv_scales + (int64_t)seq * a.cap * 32;
-  const uint8_t *swa = a.swa_kv ? a.swa_kv + ((int64_t)seq * a.swa_len) * 512 : nullptr;
-  const int32_t *topk = a.topk ? a.topk + (int64_t)r * a.k_pos : nullptr;
-
-  // Entry ids of a tile's two 16-key blocks (lane c: slots 16kb + c).  They
-  // are read ahead of need and without waiting for n_topk (every slot below
-  // k_pos is inside the row), so only the gather of the codes waits on an
-  // earlier load.
-  auto load_ids = [&](int tile, int32_t (&e)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int slot = tile * kCqTileKeys + 16 * kb + c;
-      e[kb] = (topk && slot < a.k_pos) ? topk[slot] : -1;
-    }
-  };
-  auto load_fp4 = [&](int tile, const int32_t (&ids)[2]) {
-    Fp4Tile t;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int slot = tile * kCqTileKeys + 16 * kb + c;
-      const int64_t e = slot < n_g ? ids[kb] : -1;
-      const bool ok = e >= 0 && e < a.cap;
-      t.valid[kb] = ok;
-      const int64_t el = ok ? e : 0;
-      t.a[kb] = *reinterpret_cast<const uint4 *>(kv_codes + el * 256 + 64 * w + 16 * G);
-      t.sc[kb] = *reinterpret_cast<const uint16_t *>(kv_scales + el * 32 + 8 * w + 2 * G);
-    }
-    return t;
-  };
-  auto load_swa = [&](int tile) {   // tile index within the SWA rows
-    SwaTile t;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int slot = tile * kCqTileKeys + 16 * kb + c;
-      const bool ok = slot < n_s;
-      t.valid[kb] = ok;
-      const int64_t row = ok ? s0 + slot : 0;
-      const uint4 *p = reinterpret_cast<const uint4 *>(swa + row * 512 + 128 * w + 32 * G);
-      t.a[kb] = p[0];
-      t.b[kb] = p[1];
-    }
-    return t;
-  };
-  // dequantise a wave's quarter of a tile's 32 keys to f16 (exact); skipped
-  // slots load entry 0 and are zeroed, so no stale byte pattern (e.g. a NaN
-  // code in an unwritten row) can reach the P.V product
-  auto dequant_fp4 = [&](const Fp4Tile &t, f16x8 (&kf)[2][4]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const _Float16 sa = e4m3_to_f16(t.sc[kb] & 0xFFu);
-      const _Float16 sb = e4m3_to_f16((t.sc[kb] >> 8) & 0xFFu);
-      const f16x8 va = f16x8{sa, sa, sa, sa, sa, sa, sa, sa};
-      const f16x8 vb = f16x8{sb, sb, sb, sb, sb, sb, sb, sb};
-      kf[kb][0] = e2m1x8_to_f16(t.a[kb].x) * va;
-      kf[kb][1] = e2m1x8_to_f16(t.a[kb].y) * va;
-      kf[kb][2] = e2m1x8_to_f16(t.a[kb].z) * vb;
-      kf[kb][3] = e2m1x8_to_f16(t.a[kb].w) * vb;
-      if (!t.valid[kb]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kf[kb][q] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-  };
-  auto dequant_swa = [&](const SwaTile &t, f16x8 (&kf)[2][4]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      kf[kb][0] = e4m3x8_to_f16(t.a[kb].x, t.a[kb].y);
-      kf[kb][1] = e4m3x8_to_f16(t.a[kb].z, t.a[kb].w);
-      kf[kb][2] = e4m3x8_to_f16(t.b[kb].x, t.b[kb].y);
-      kf[kb][3] = e4m3x8_to_f16(t.b[kb].z, t.b[kb].w);
-      if (!t.valid[kb]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) kf[kb][q] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-  };
-
-  // the first three global tiles' ids are read before n_topk arrives
-  // (t_begin does not depend on it); slots past the row's count are masked in
-  // load_fp4
-  int32_t id0[2], id1[2], id2[2];
-  load_ids(t_begin, id0);
-  load_ids(t_begin + 1, id1);
-  load_ids(t_begin + 2, id2);
-  const int g_end = t_end < n_gt ? t_end : n_gt;      // global tiles: [t_begin, g_end)
-  Fp4Tile ta, tb, tc;
-  if (t_begin < g_end) ta = load_fp4(t_begin, id0);
-  if (t_begin + 1 < g_end) tb = load_fp4(t_begin + 1, id1);
-
-  // One tile of dequantised keys: partial logits, online softmax, P.V.
-  auto compute_tile = [&](const f16x8 (&kf)[2][4], const bool (&valid)[2]) {
-    if (w == 0 && G == 0) {
-      s_valid[c] = valid[0];
-      s_valid[16 + c] = valid[1];
-    }
-
-    // partial logits over this wave's channel quarter
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) s = mfma16x16x32(qa[hb][t], kf[kb][t], s);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_part[w][16 * hb + 4 * G + i][16 * kb + c] = s[i];
-      }
-    // this wave's dequantised quarter, natural layout [key][channel]; the P.V
-    // product reads it back transposed
-    _Float16 *vn = &s_vn[w][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        *reinterpret_cast<f16x8 *>(vn + (16 * kb + c) * kVnStride + 32 * G + 8 * t) = kf[kb][t];
-    __syncthreads();
-
-    // online softmax: thread -> head h, keys kk0 .. kk0 + KPT - 1
-    {
-      const int h = tid / TPH;
-      const int kk0 = (tid % TPH) * KPT;
-      float sv[KPT];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int kk = kk0 + j;
-        float s = (s_part[0][h][kk] + s_part[1][h][kk]) + (s_part[2][h][kk] + s_part[3][h][kk]);
-        s = s_valid[kk] ? s * a.scale_log2 : -INFINITY;
-        sv[j] = s;
-        tmax = fmaxf(tmax, s);
-      }
-      tmax = group_max<TPH>(tmax);
-      float m_new = m_run;
-      if (m_run == -INFINITY || tmax > m_run + kLazyRescale) m_new = fmaxf(tmax, m_run);
-      // the hardware exp2 (no denormal-range fix-up): arguments are <= 2^8,
-      // and results below 2^-126 are negligible weights (f16 drops them too)
-      const float alpha = (m_run == -INFINITY || m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      float psum = 0.f;
-      _Float16 ph[KPT];
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const float p = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_new);
-        ph[j] = (_Float16)p;
-        psum += (float)ph[j];
-      }
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) s_p[h * kPStride + kk0 + j] = ph[j];
-      l_thr = l_thr * alpha + psum;
-      m_run = m_new;
-      if ((tid % TPH) == 0) s_alpha[h] = alpha;
-    }
-    __syncthreads();
-
-    // O[:, quarter] = alpha * O + P V (the rescale is skipped while the
-    // running maxima of this wave's heads stand still)
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const float4 al = *reinterpret_cast<const float4 *>(&s_alpha[16 * hb + 4 * G]);
-      const bool move = al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f;
-      if (__builtin_amdgcn_ballot_w64(move)) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          acc_o[hb][db][0] *= al.x;
-          acc_o[hb][db][1] *= al.y;
-          acc_o[hb][db][2] *= al.z;
-          acc_o[hb][db][3] *= al.w;
-        }
-      }
-    }
-    // B operand of channel block db: keys 8G .. 8G+7 at channel 16db + c.
-    // Lane (G, c) addresses row 8G + 4h + c/4, channels 16db + 4 (c % 4) of
-    // the two 4-key halves h.
-    // (read two channel blocks at a time, to bound the registers they hold)
-    const _Float16 *r0 = vn + (8 * G + (c >> 2)) * kVnStride + 4 * (c & 3);
-    const _Float16 *r1 = r0 + 4 * kVnStride;
-    f16x8 pa[HB];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) pa[hb] = *reinterpret_cast<const f16x8 *>(&s_p[(16 * hb + c) * kPStride + 8 * G]);
-#pragma unroll
-    for (int db = 0; db < 8; db += 2) {
-      f16x8 vb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f16x4 lo = lds_read_tr16(r0 + 16 * (db + u));
-        const f16x4 hi = lds_read_tr16(r1 + 16 * (db + u));
-        vb[u] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) acc_o[hb][db + u] = mfma16x16x32(pa[hb], vb[u], acc_o[hb][db + u]);
-    }
-    __syncthreads();
-  };
-
-  // Global tiles: while a tile is computed the next two are in flight (the
-  // gathers are random HBM reads); the three tile registers rotate by copy.
-  f16x8 kf[2][4];
-  for (int tile = t_begin; tile < g_end; ++tile) {
-    int32_t idn[2] = {-1, -1};
-    if (tile + 2 < g_end) tc = load_fp4(tile + 2, id2);
-    if (tile + 3 < g_end) load_ids(tile + 3, idn);
-    dequant_fp4(ta, kf);
-    compute_tile(kf, ta.valid);
-    ta = tb;
-    tb = tc;
-    id2[0] = idn[0];
-    id2[1] = idn[1];
-  }
-  // SWA tiles (consecutive rows), the next one in flight
-  {
-    const int sw_begin = (t_begin > n_gt ? t_begin : n_gt) - n_gt;
-    const int sw_end = t_end - n_gt;
-    SwaTile sa, sb;
-    if (sw_begin < sw_end) sa = load_swa(sw_begin);
-    for (int st = sw_begin; st < sw_end; ++st) {
-      if (st + 1 < sw_end) sb = load_swa(st + 1);
-      dequant_swa(sa, kf);
-      compute_tile(kf, sa.valid);
-      sa = sb;
-    }
-  }
-
-  {
-    const float l = group_sum<TPH>(l_thr);
-    if ((tid % TPH) == 0) {
-      s_m[tid / TPH] = m_run;
-      s_l[tid / TPH] = l;
-    }
-  }
-  __syncthreads();
-  if (split) {
-    // unnormalised partial: O, running max (log2 units) and sum per head
-    const int64_t part = (int64_t)r * a.n_split + sp;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 16 * hb + 4 * G + i;
-        float *prow = a.part_o + (part * HT + h0 + h) * 512 + 128 * w + c;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) prow[16 * db] = acc_o[hb][db][i];
-      }
-    if (tid < H) {
-      a.part_ml[(part * HT + h0 + tid) * 2] = s_m[tid];
-      a.part_ml[(part * HT + h0 + tid) * 2 + 1] = s_l[tid];
-    }
-    return;
-  }
-  // normalise and store
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * hb + 4 * G + i;
-      const float l = s_l[h];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      float *orow = a.o + ((int64_t)r * HT + h0 + h) * 512 + 128 * w + c;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) orow[16 * db] = acc_o[hb][db][i] * inv;
-    }
-  }
-  if (tid < H) {
-    const float l = s_l[tid];
-    a.lse[(int64_t)r * HT + h0 + tid] =
-        l > 0.f ? (s_m[tid] + log2f(l)) * 0.6931471805599453f : -INFINITY;
-  }
-}
-
 // Merge of the split partials of a row: the softmax over the union of the
 // splits' key sets (and of the earlier result in (o, lse) when merge_in is
 // set), by their log-sum-exp.  A block handles 2 heads x 512 channels of one
@@ -925,7 +486,7 @@ hipError_t prepare_attention() { return hipSuccess; }
 
 AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t window) {
   // keys per tile of the kernel that serves this head count
-  const int tk = n_heads == 64 ? kCqTileKeys : kAttnTileKeys;
+  const int tk = n_heads == 64 ? 32 : kAttnTileKeys;
   const int max_tiles = (k_pos + tk - 1) / tk + (window + tk - 1) / tk;
   AttnPlan p = {1, max_tiles > 0 ? max_tiles : 1, 0};
   // Few rows leave most of the 256 CUs idle: spread each row's key tiles over

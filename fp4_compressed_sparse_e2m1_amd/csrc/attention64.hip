@@ -109,6 +109,16 @@ attn_h64_kernel(AttnArgs a) {
   load_ids(t_begin + 3, n0);
   load_ids(t_begin + 4, n1);
   load_ids(t_begin + 5, n2);
+  // then Q (bf16, converted once the first gathers are out: the load counter
+  // is in order, so waiting for Q does not wait for them)
+  uint4 q_raw[4][4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * H + 16 * hb + c) * 512 + 128 * q + 32 * G);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) q_raw[hb][t] = qp[t];
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // the per-row scalars are read together (none waits on another)
   int seq = a.row_seq[r];
@@ -206,11 +216,9 @@ attn_h64_kernel(AttnArgs a) {
   // order)
   f16x8 qa[4][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * H + 16 * hb + c) * 512 + 128 * q + 32 * G);
+  for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qa[hb][t] = bf16x8_to_f16(qp[t]);
-  }
+    for (int t = 0; t < 4; ++t) qa[hb][t] = bf16x8_to_f16(q_raw[hb][t]);
 
   // O^T accumulators: acc[hb][db] lane (G, c) holds
   // O[16hb + c][64w + 16db + 4G + i]
