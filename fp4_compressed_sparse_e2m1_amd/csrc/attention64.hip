@@ -41,6 +41,9 @@ constexpr int kKeys = 32;              // keys per tile
 constexpr int kSPS = 32 + 4;           // floats per partial-logit row (one head, 32 keys + pad)
 constexpr int kVS = 128 + 8;           // halves per LDS key row (a quarter's 128 channels + pad)
 constexpr int kPS = 32 + 8;            // halves per P row
+// scheduling-fence mask: ALU, transcendental and LDS instructions may be
+// moved across the fence, global-memory instructions may not
+constexpr int kAllButVmem = 0x0001 | 0x0080 | 0x0400;
 
 // A lane's raw share of one key block (key c of block h2, the lane's 32
 // channels of quarter q): the E2M1 codes in a and the key's two scale bytes
@@ -247,6 +250,10 @@ attn_h64_kernel(AttnArgs a) {
       m_run = lin * 1.4426950408889634f;
       l_thr = lane < 8 ? 1.f : 0.f;
     }
+    // Wait for the earlier result here: otherwise the first use of the
+    // accumulators inside the loop would carry a wait for every load in flight
+    // (the count cannot tell these loads apart from the gathers), on every pass.
+    __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
   }
 
   uint32_t mask = 0;        // present keys of the tile whose logits are in s_part
@@ -375,15 +382,16 @@ attn_h64_kernel(AttnArgs a) {
   // by three so every slot is a fixed set of registers.
   if (has_tiles) {
     // A(T + 1) from slot nxt, then the loads that refill it
+    // (the fences let arithmetic and LDS work move across them, not loads)
     auto advance = [&](int T, Slot &nxt) {
       stage_a(T + 1, nxt.t, bh);
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(kAllButVmem);
       bh = load_hi(T + 2);
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(kAllButVmem);
       nxt.t = load_raw(T + 4, nxt.nid);
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(kAllButVmem);
       load_ids(T + 7, nxt.nid);
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(kAllButVmem);
     };
     advance(t_begin - 1, sl0);
     __syncthreads();
