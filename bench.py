@@ -48,9 +48,9 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "9d542c5da7091519d19c0441fbb8e0c78f5c40f161ccb1deb29d482a0a7c29a1",
-    "fetch_kib": 278648.885, "fetch_scale": 524288 / 262166.75,
-    "write_kib": 4172.156, "write_scale": 524288 / 524288.0,
+    "sha256": "f5817f0d6864476d354cc5ca23aaeb1fb62419a2c7c2d5bb6ae29cba4846d3c6",
+    "fetch_kib": 278648.938, "fetch_scale": 524288 / 262166.625,
+    "write_kib": 4175.792, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -327,7 +327,7 @@ def reuse_attention(steps, warmup):
     per_query = 512 * 288 + wl.swa * 512 + H * 1024 + 512 * 4 + H * 2048 + H * 4
     achieved = per_query * B / (us * 1e-6) / 1e9
     del cache
-    return {"workload": wl.name, "kernel": "attn_kernel<64 heads> (csa2_sparse_attn, SWA fused)",
+    return {"workload": wl.name, "kernel": "attn_h64_kernel (csa2_sparse_attn, 64 heads, SWA fused)",
             "avg_launch_us": round(us, 2), "query_tokens_per_s": round(B / (us * 1e-6), 1),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": per_query * B}}
