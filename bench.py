@@ -54,17 +54,35 @@ SCAN_COUNTERS = {
 }
 
 
+# The same two counters for the 64-head attention at batch 256 (bench.py
+# --attention-only: 23 launches; profiles/attn_h64_kernel_reuse_b256_hbm_counters.txt), scaled
+# by the same copy calibration.
+ATTN64_COUNTERS = {
+    "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
+                "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
+                "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
+    "sha256": "1c9b02fb35b2d1d99b492618019a92426dff3f319962445d2713dcad4a562fd3",
+    "fetch_kib": 46186.266, "fetch_scale": 524288 / 262166.625,
+    "write_kib": 32833.394, "write_scale": 524288 / 524288.0,
+}
+
+
+def counter_traffic_bytes(c):
+    """Counter-measured HBM bytes per launch, or None when the kernel's
+    sources changed since the counters were taken."""
+    h = hashlib.sha256()
+    for f in c["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != c["sha256"]:
+        return None
+    return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
+
+
 def scan_traffic_bytes():
     """Counter-measured HBM bytes per scan launch, or None when the scan's
     sources changed since the counters were taken."""
-    h = hashlib.sha256()
-    for f in SCAN_COUNTERS["sources"]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest() != SCAN_COUNTERS["sha256"]:
-        return None
-    c = SCAN_COUNTERS
-    return int(round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024))
+    return counter_traffic_bytes(SCAN_COUNTERS)
 SCALE = 1.0 / math.sqrt(512)
 
 
@@ -78,6 +96,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention-roofline", action="store_true",
                     help="skip the batch-256, 64-head attention bandwidth measurement")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="run only the batch-256, 64-head attention measurement and print its object "
+                         "(for profiling that kernel; not the benchmark line)")
     ap.add_argument("--ctx", type=int, default=None, help="override the context (testing only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB buffer once with a plain device copy "
@@ -330,7 +351,8 @@ def reuse_attention(steps, warmup):
     return {"workload": wl.name, "kernel": "attn_h64_kernel (csa2_sparse_attn, 64 heads, SWA fused)",
             "avg_launch_us": round(us, 2), "query_tokens_per_s": round(B / (us * 1e-6), 1),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": per_query * B}}
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic_bytes(ATTN64_COUNTERS),
+                         "algorithmic_bytes_per_launch": per_query * B}}
 
 
 def copy_bandwidth():
@@ -458,6 +480,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.attention_only:
+        print(json.dumps(reuse_attention(args.steps, args.warmup)))
+        return
     t_build = time.perf_counter()
     c = build(args.ctx)
     t_build = time.perf_counter() - t_build
