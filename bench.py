@@ -108,13 +108,16 @@ def parse():
     return ap.parse_args()
 
 
-def build(ctx_override=None):
+def build(ctx_override=None, wid=3):
+    """Builds a decode workload (the 1M-context stack by default): its FP4
+    cache of T - 1 entries per sequence, the step's new entries, and every
+    layer's queries, SWA windows and outputs."""
     import torch
 
     import fp4_compressed_sparse_e2m1_amd as csa2
     import workloads as W
 
-    wl = W.WORKLOADS[3]
+    wl = W.WORKLOADS[wid]
     B, T, H = wl.batch, ctx_override or wl.ctx, wl.heads
     dev = "cuda"
     seed = wl.seed
@@ -353,6 +356,124 @@ def reuse_attention(steps, warmup):
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic_bytes(ATTN64_COUNTERS),
                          "algorithmic_bytes_per_launch": per_query * B}}
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+
+
+def _event_pairs(n):
+    import torch
+
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def prefill_chunk(steps, warmup):
+    """The encoder Full-mode prefill chunk: 4,096 new query tokens (t = 61,440
+    .. 65,535) against a 65,536-token context stored at 2 tokens -> 1 entry
+    (32,768 FP4 entries), each query scoring its causally visible entries
+    (entry j visible to token t iff 2j + 1 <= t) and keeping a flat Top-512,
+    then 16-head sparse attention over those entries with the last 128
+    tokens' FP8 SWA rows in the same softmax.  The scoring and attention
+    contractions are dense, so the roof is the matrix-core one: useful flops =
+    2 x 8 x 128 per (query, visible entry) for the scores + 2 x 2 x 16 x 512
+    per (query, attended key) for Q.K and P.V."""
+    import numpy as np
+    import torch
+
+    import fp4_compressed_sparse_e2m1_amd as csa2
+    import workloads as W
+
+    wl = W.WORKLOADS[1]
+    seed, H = wl.seed, wl.heads
+    n_ent = wl.ctx // wl.entry_ratio
+    t = np.arange(wl.ctx - wl.chunk, wl.ctx)
+    n_vis = (t + 1) // 2
+    R = len(t)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device="cuda")
+    cache = csa2.Cache(1, n_ent)
+    lat = W.rms_rows(n_ent, 512, W.seed_for(seed, W.T_LATENT), device="cuda")
+    ik = W.rms_rows(n_ent, 128, W.seed_for(seed, W.T_IKEY), device="cuda")
+    csa2.csa2_quantize_fp4(lat, 16, cache.kv_codes, cache.kv_scales)
+    csa2.csa2_quantize_fp4(ik, 32, cache.ik_codes, cache.ik_scales)
+    del lat, ik
+    q_idx = W.bf16_normal((R, 8, 128), W.seed_for(seed, W.T_QIDX), device="cuda")
+    w = W.uniform01((R, 8), W.seed_for(seed, W.T_W), device="cuda")
+    seqs, nvis = i32([0] * R), i32(n_vis)
+    max_nvis = int(n_vis.max())
+    topk = torch.empty((R, wl.k_pos), dtype=torch.int32, device="cuda")
+    ntopk = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(csa2.CSA2_OP_INDEX_FULL, R, max_nvis, 0, wl.k_pos)
+    swa_first = int(t[0]) - (wl.swa - 1)
+    swa_kv = W.swa_rows_e4m3(int(t[-1]) - swa_first + 1, 512, W.seed_for(seed, W.T_SWA),
+                             device="cuda").reshape(1, -1, 512)
+    swa = csa2.Swa(swa_kv, i32(t - swa_first + 1), wl.swa)
+    q = W.bf16_normal((R, H, 512), W.seed_for(seed, W.T_Q), device="cuda")
+    o = torch.empty((R, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    wsa = csa2.attn_workspace(R, H, wl.k_pos, wl.swa)
+
+    def index():
+        csa2.csa2_index_full(cache, q_idx, w, seqs, nvis, max_nvis, 0, wl.k_pos, None, None, topk, ntopk, ws)
+
+    def attend():
+        csa2.csa2_sparse_attn(cache, q, seqs, topk, ntopk, SCALE, o, lse, swa=swa, workspace=wsa)
+
+    for _ in range(warmup):
+        index()
+        attend()
+    ev_i, ev_a = _event_pairs(steps), _event_pairs(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev_i[k][0].record()
+        index()
+        ev_i[k][1].record()
+        ev_a[k][0].record()
+        attend()
+        ev_a[k][1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    idx_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev_i) / steps
+    att_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev_a) / steps
+    keys = int(ntopk.sum().item()) + R * wl.swa
+    score_flop = 2 * 8 * 128 * int(n_vis.sum())
+    attn_flop = 2 * 2 * H * 512 * keys
+    tf = lambda f, us: f / (us * 1e-6) / 1e12
+    del cache
+    return {"workload": wl.name, "query_tokens": R, "context_entries": n_ent,
+            "query_tokens_per_s": round(R / wall, 1), "ms_per_chunk": round(wall * 1e3, 3),
+            "index_us": round(idx_us, 1), "attention_us": round(att_us, 1),
+            "roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": MFMA_F16_PEAK_TFLOPS,
+                         "index": {"achieved": round(tf(score_flop, idx_us), 1),
+                                   "frac": round(tf(score_flop, idx_us) / MFMA_F16_PEAK_TFLOPS, 4),
+                                   "flop": score_flop},
+                         "attention": {"achieved": round(tf(attn_flop, att_us), 1),
+                                       "frac": round(tf(attn_flop, att_us) / MFMA_F16_PEAK_TFLOPS, 4),
+                                       "flop": attn_flop}}}
+
+
+def decode_b32(steps, warmup):
+    """The 128K-context decode step at batch 32: append, a Full layer (scan of
+    131,072 entries, 2,048 blocks -> 16,384-candidate pool -> Top-512,
+    attention + SWA) and 18 Reindex layers (re-score the pool with their own
+    indexer query, Top-512, attention + SWA)."""
+    c = build(wid=2)
+    wall, scan_ms, per_layer = run_gpu(c, steps, warmup, True)
+    B, T, L = c["B"], c["T"], c["L"]
+    scan_bytes = IK_BYTES * T * B + BLOCK_KEY_BYTES * ((T + 7) // 8) * B
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    modes = c["wl"].layers
+    mode_us = {m: 1e3 * sum(t for t, mm in zip(per_layer, modes) if mm == m) /
+               max(1, sum(1 for mm in modes if mm == m)) for m in ("full", "reindex")}
+    out = {"workload": c["wl"].name, "batch": B, "context_entries": T, "layers": L,
+           "query_tokens_per_s_per_layer": round(B * L / (wall / steps), 1),
+           "ms_per_step": round(wall * 1e3 / steps, 4),
+           "per_layer_us_eager": {k: round(v, 2) for k, v in mode_us.items()},
+           "scan": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": scan_bytes,
+                    "avg_launch_us": round(scan_ms * 1e3, 2)}}
+    del c
+    return out
 
 
 def copy_bandwidth():

@@ -44,6 +44,10 @@ namespace csa2 {
 namespace {
 
 constexpr int kScoreThreads = 256;
+// Flat scoring of at least this many rows shares each key tile among 8 rows.
+constexpr int kScoreRowsMin = 16;
+// Entries per work-group of the many-row flat scoring (32 tiles per wave).
+constexpr int kScoreRowsChunk = 2048;
 
 // Entries per work-group: long contiguous runs for the scan, short ones for the
 // pool gather (its pool-id -> key loads form a dependent chain).
@@ -179,6 +183,178 @@ score_kernel(ScoreArgs a) {
     run(std::true_type{});
   else
     run(std::false_type{});
+}
+
+// Flat scoring of many query rows (prefill: consecutive query tokens of one
+// sequence).  A work-group takes kRows = 2 * RP consecutive rows and one chunk
+// of entries.  Each 16-entry tile is loaded and dequantised once and
+// multiplied against every pair of rows: MFMA rows 0..7 are the first row's 8
+// heads and rows 8..15 the second row's, so no matrix row is padding and the
+// key reads and conversions are shared by the work-group's rows.  Rows of one
+// work-group that belong to different sequences are scored one sequence at a
+// time (each pass covers the rows of one sequence).
+template <int RP>
+__global__ void __launch_bounds__(kScoreThreads)
+score_rows_kernel(ScoreArgs a, int32_t n_rows) {
+  static_assert(RP % 2 == 0, "row pairs are combined two at a time");
+  constexpr int kRows = 2 * RP;
+  constexpr int kTilesPerWave = kScoreRowsChunk / (4 * 16);
+  constexpr int U = 4;
+  const int r0 = blockIdx.y * kRows;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kScoreRowsChunk;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int G = lane >> 4;
+  const int c = lane & 15;
+
+  int seq[kRows], nv[kRows];
+  uint32_t pending = 0;
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int r = r0 + i;
+    seq[i] = -1;
+    nv[i] = 0;
+    if (r < n_rows) {
+      const int s = a.row_seq[r];
+      int n = a.row_nvis[r];
+      n = n < 0 ? 0 : (n > a.max_nvis ? a.max_nvis : n);
+      if (s < 0 || s >= a.n_seq) n = 0;
+      seq[i] = s;
+      nv[i] = n;
+      if (n > chunk0) pending |= 1u << i;
+    }
+  }
+  if (!pending) return;
+
+  // Query operand of pair p: lane (G, c) holds MFMA row c = head (c & 7) of
+  // row 2p + (c >> 3), channels 32G + 8t .. +7 for step t.
+  f16x8 qa[RP][4];
+  // Output side: lane (G, c) ends with MFMA rows 4G .. 4G+3 = heads
+  // 4(G & 1) .. +3 of row 2p + (G >> 1), entry c.
+  float wh[RP][4];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    const int rq = r0 + 2 * p + (c >> 3);
+    if (rq < n_rows) {
+      const uint4 *qp = reinterpret_cast<const uint4 *>(a.q_idx + ((int64_t)rq * 8 + (c & 7)) * 128 + 32 * G);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qa[p][t] = bf16x8_to_f16(qp[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qa[p][t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    const int rw = r0 + 2 * p + (G >> 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wh[p][i] = rw < n_rows ? a.w[(int64_t)rw * 8 + 4 * (G & 1) + i] : 0.f;
+  }
+
+  while (pending) {
+    const int lead = __builtin_ctz(pending);
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i)
+      if (i == lead) s = seq[i];
+    uint32_t act = 0;
+    int nmax = 0, nmin = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      if (((pending >> i) & 1u) && seq[i] == s) {
+        act |= 1u << i;
+        nmax = nv[i] > nmax ? nv[i] : nmax;
+        nmin = nv[i] < nmin ? nv[i] : nmin;
+      }
+    }
+    pending &= ~act;
+    // Two row pairs share one epilogue: lane (G, c) ends with the score of
+    // row 2p + 2(G & 1) + (G >> 1) (p even), entry c, and writes it when that
+    // row is in this pass and the entry is below its n_vis.
+    int wr_nv[RP / 2];
+    uint32_t *out[RP / 2];
+#pragma unroll
+    for (int p2 = 0; p2 < RP / 2; ++p2) {
+      const int i = 4 * p2 + 2 * (G & 1) + (G >> 1);
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < kRows; ++j)
+        if (j == i) n = nv[j];
+      wr_nv[p2] = ((act >> i) & 1u) ? n : 0;
+      out[p2] = a.keys_out + (int64_t)(r0 + i) * a.out_stride;
+    }
+    const int slot00 = (int)chunk0 + wave * kTilesPerWave * 16 + c;
+    const uint8_t *codes_base = a.ik_codes + (int64_t)s * a.cap * 64;
+    const uint8_t *scales_base = a.ik_scales + (int64_t)s * a.cap * 4;
+    auto run = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      // batch of U tiles starting at tile tb: raw code and scale loads
+      auto load = [&](int tb, uint4 *craw, uint32_t *sraw) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = slot00 + (tb + u) * 16;
+          const int e_ld = (FULL || e < nmax) ? e : 0;
+          craw[u] = *reinterpret_cast<const uint4 *>(codes_base + (int64_t)e_ld * 64 + 16 * G);
+          sraw[u] = scales_base[(int64_t)e_ld * 4 + G];
+        }
+      };
+      auto compute = [&](int tb, const uint4 *craw, const uint32_t *sraw) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = slot00 + (tb + u) * 16;
+          const _Float16 sc = e4m3_to_f16(sraw[u]);
+          const f16x8 sv = f16x8{sc, sc, sc, sc, sc, sc, sc, sc};
+          const f16x8 k0 = e2m1x8_to_f16(craw[u].x) * sv;
+          const f16x8 k1 = e2m1x8_to_f16(craw[u].y) * sv;
+          const f16x8 k2 = e2m1x8_to_f16(craw[u].z) * sv;
+          const f16x8 k3 = e2m1x8_to_f16(craw[u].w) * sv;
+          f32x4 acc[RP];
+#pragma unroll
+          for (int p = 0; p < RP; ++p) {
+            acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[p] = mfma16x16x32(qa[p][0], k0, acc[p]);
+            acc[p] = mfma16x16x32(qa[p][1], k1, acc[p]);
+            acc[p] = mfma16x16x32(qa[p][2], k2, acc[p]);
+            acc[p] = mfma16x16x32(qa[p][3], k3, acc[p]);
+          }
+#pragma unroll
+          for (int p2 = 0; p2 < RP / 2; ++p2) {
+            float pa = wh[2 * p2][0] * relu(acc[2 * p2][0]) + wh[2 * p2][1] * relu(acc[2 * p2][1]);
+            pa += wh[2 * p2][2] * relu(acc[2 * p2][2]) + wh[2 * p2][3] * relu(acc[2 * p2][3]);
+            float pb = wh[2 * p2 + 1][0] * relu(acc[2 * p2 + 1][0]) + wh[2 * p2 + 1][1] * relu(acc[2 * p2 + 1][1]);
+            pb += wh[2 * p2 + 1][2] * relu(acc[2 * p2 + 1][2]) + wh[2 * p2 + 1][3] * relu(acc[2 * p2 + 1][3]);
+            // heads 0..3 + heads 4..7 of one row per lane: even G keeps its
+            // own pair, odd G the next
+            const bool odd = (G & 1) != 0;
+            const float x = odd ? pb : pa;
+            const float y = odd ? pa : pb;
+            const float score = x + swap_rows16(y);
+            if (e < wr_nv[p2]) out[p2][e] = score_key(score);
+          }
+        }
+      };
+      // tiles of this wave that hold entries below nmax
+      int n_tiles = kTilesPerWave;
+      if (!FULL) {
+        const int left = nmax - (slot00 - c);
+        n_tiles = left <= 0 ? 0 : (left >= kTilesPerWave * 16 ? kTilesPerWave : (left + 15) / 16);
+      }
+      if (n_tiles == 0) return;
+      // two batches in flight: the next batch's loads are issued before the
+      // current batch is converted and multiplied
+      uint4 ca[U], cb[U];
+      uint32_t sa_[U], sb[U];
+      load(0, ca, sa_);
+      for (int tb = 0; tb < n_tiles; tb += 2 * U) {
+        if (tb + U < n_tiles) load(tb + U, cb, sb);
+        compute(tb, ca, sa_);
+        if (tb + U >= n_tiles) break;
+        if (tb + 2 * U < n_tiles) load(tb + 2 * U, ca, sa_);
+        compute(tb + U, cb, sb);
+      }
+    };
+    if (chunk0 + kScoreRowsChunk <= nmin)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+  }
 }
 
 // ------------------------------------------------------------- selection
@@ -701,6 +877,12 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int6
   const int chunk = mode == kScorePool ? kScorePoolChunk : kScoreChunk;
   const int64_t chunks = (slots + chunk - 1) / chunk;
   if (chunks == 0 || n_rows == 0) return hipSuccess;
+  if (mode == kScoreFlat && n_rows >= kScoreRowsMin && slots <= ((int64_t)1 << 30)) {
+    constexpr int kRP = 4;
+    dim3 grid((unsigned)((slots + kScoreRowsChunk - 1) / kScoreRowsChunk), (unsigned)((n_rows + 2 * kRP - 1) / (2 * kRP)));
+    score_rows_kernel<kRP><<<grid, kScoreThreads, 0, stream>>>(a, n_rows);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)chunks, (unsigned)n_rows);
   switch (mode) {
     case kScoreBlockMax: score_kernel<kScoreBlockMax><<<grid, kScoreThreads, 0, stream>>>(a); break;

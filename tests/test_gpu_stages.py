@@ -201,6 +201,33 @@ def test_index_full_flat_mode(csa2, n_vis_rows):
         check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], "flat")
 
 
+def test_index_flat_many_rows(csa2):
+    """Flat scoring of many rows at once (the prefill shape: consecutive query
+    tokens of one sequence, n_vis growing by one per row), with work-groups
+    whose rows mix sequences, an empty row, an out-of-range sequence id, a
+    one-entry row and a row count that is not a multiple of the row group."""
+    n_list = [5000, 3001]
+    cache, ora = make_index_case(csa2, n_list, 5000, seed=41)
+    rows = [(0, 4970 + i) for i in range(30)]
+    rows[12] = (1, 3001)
+    rows[13] = (1, 2999)
+    rows += [(1, 3001), (0, 0), (7, 100), (1, 1), (0, 4999), (0, 512), (0, 513)]
+    R, k_pos = len(rows), 512
+    qidx = W.bf16_normal((R, 8, 128), seed=42)
+    w = W.uniform01((R, 8), seed=43)
+    _, _, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [s for s, _ in rows],
+                                 [n for _, n in rows], max(n for _, n in rows), 0, k_pos)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    for r, (s, nv) in enumerate(rows):
+        if s >= len(n_list) or nv == 0:
+            assert ntopk[r] == 0 and np.all(topk[r] == -1), r
+            continue
+        _, _, ikc, iks = ora[s]
+        ref = oracle.full_layer_select(qb[r], wn[r], ikc, iks, nv, 0, k_pos)
+        sc = ref["entry_scores"]
+        check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], f"row {r}")
+
+
 @pytest.mark.parametrize("kind", ["outlier", "tied_block", "narrow_spread"])
 def test_index_flat_selection_regimes(csa2, kind):
     """Score distributions that steer the selection off its common case:
