@@ -24,6 +24,10 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int plan_levels(int64_t n_max, int k, int64_t *chunks) {
   int levels = 0;
   int64_t n = n_max;
+  if (n <= kSelectChunkWide) {     // one level (the wide selection above kSelectChunk keys)
+    chunks[0] = 1;
+    return 1;
+  }
   while (n > kSelectChunk && levels < 7) {
     const int64_t ch = (n + kSelectChunk - 1) / kSelectChunk;
     chunks[levels++] = ch;
@@ -132,7 +136,7 @@ hipError_t run_select(const uint32_t *keys, int64_t stride, int count_kind, int 
       a.keys_out = reinterpret_cast<uint32_t *>(buf);
       a.ids_out = reinterpret_cast<int32_t *>(buf + half / 2);
       a.out_stride = out_stride;
-      hipError_t e = launch_select(a, rows, (int32_t)chunks[l], false, stream);
+      hipError_t e = launch_select(a, rows, (int32_t)chunks[l], false, false, stream);
       if (e != hipSuccess) return e;
       kin = a.keys_out;
       iin = a.ids_out;
@@ -146,7 +150,9 @@ hipError_t run_select(const uint32_t *keys, int64_t stride, int count_kind, int 
       a.pool_blocks = fin.pool_blocks;
       a.n_pool = fin.n_pool;
       a.k_blocks = fin.k_blocks;
-      hipError_t e = launch_select(a, rows, 1, true, stream);
+      // a single level over more keys than one chunk: the wide selection
+      const bool wide = levels == 1 && n_max > kSelectChunk;
+      hipError_t e = launch_select(a, rows, 1, true, wide, stream);
       if (e != hipSuccess) return e;
     }
   }

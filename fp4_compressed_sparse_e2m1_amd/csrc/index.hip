@@ -461,9 +461,15 @@ __device__ __forceinline__ Digit find_digit(const uint32_t *hist, int nb, int k_
   return d;
 }
 
-template <bool FINAL, bool IDS>
+// KPT keys per thread: a work-group holds up to kSelThreads * KPT keys of a
+// row (16: the chunk of the multi-level selection; 32: a whole row of up to
+// 32,768 keys in one level).
+template <bool FINAL, bool IDS, int KPT = kKeysPerThread>
 __global__ void __launch_bounds__(kSelThreads)
 select_kernel(SelectArgs a) {
+  constexpr int kKeys = KPT;
+  constexpr int kSpan = 64 * KPT;
+  constexpr int kChunkKeys = kSelThreads * KPT;
   __shared__ __attribute__((aligned(16))) uint32_t hist[kSelBins];
   __shared__ uint32_t s_lkey[kListCap];   // the list's keys; the candidates of the generic path
   __shared__ int32_t s_lid[kListCap];
@@ -490,28 +496,28 @@ select_kernel(SelectArgs a) {
     if (seq < 0 || seq >= a.n_seq) nv = 0;
     n_row = (a.count_kind == kCountNvis) ? nv : (nv + 7) / 8;
   }
-  const int64_t start = (int64_t)chunk * kSelectChunk;
+  const int64_t start = (int64_t)chunk * kChunkKeys;
   int n = (int)((int64_t)n_row - start);
-  n = n < 0 ? 0 : (n > kSelectChunk ? kSelectChunk : n);
+  n = n < 0 ? 0 : (n > kChunkKeys ? kChunkKeys : n);
 
   // keys (and carried ids) into registers.  The loads are bounded by the
   // row's stride, which the host knows, not by the row's count n, so they do
   // not wait for the count; positions at or past n are cleared afterwards.
   const uint32_t *kin = a.keys_in + (int64_t)r * a.in_stride + start;
   const int64_t in_left = a.in_stride - start;
-  const int n_ld = in_left < kSelectChunk ? (int)in_left : kSelectChunk;
-  const int base = wave * kSelSpan + lane;
-  uint32_t key[kKeysPerThread];
+  const int n_ld = in_left < kChunkKeys ? (int)in_left : kChunkKeys;
+  const int base = wave * kSpan + lane;
+  uint32_t key[kKeys];
 #pragma unroll
-  for (int j = 0; j < kKeysPerThread; ++j) {
+  for (int j = 0; j < kKeys; ++j) {
     const int i = base + 64 * j;
     key[j] = i < n_ld ? kin[i] : 0u;
   }
-  int32_t ids[IDS ? kKeysPerThread : 1];
+  int32_t ids[IDS ? kKeys : 1];
   if (IDS) {
     const int32_t *idin = a.ids_in + (int64_t)r * a.in_stride + start;
 #pragma unroll
-    for (int j = 0; j < kKeysPerThread; ++j) {
+    for (int j = 0; j < kKeys; ++j) {
       const int i = base + 64 * j;
       ids[j] = i < n_ld ? idin[i] : -1;
     }
@@ -525,7 +531,7 @@ select_kernel(SelectArgs a) {
     np = np < 0 ? 0 : (np > a.k_blocks ? a.k_blocks : np);
   }
 #pragma unroll
-  for (int j = 0; j < kKeysPerThread; ++j) {
+  for (int j = 0; j < kKeys; ++j) {
     if (base + 64 * j >= n) {
       key[j] = 0u;
       if (IDS) ids[j] = -1;
@@ -534,7 +540,7 @@ select_kernel(SelectArgs a) {
   // count, min and max of the valid (non-zero) keys
   uint32_t nvalid = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int j = 0; j < kKeysPerThread; ++j) {
+  for (int j = 0; j < kKeys; ++j) {
     nvalid += key[j] != 0u;
     if (key[j] != 0u) kmin = kmin < key[j] ? kmin : key[j];
     kmax = kmax > key[j] ? kmax : key[j];
@@ -602,7 +608,7 @@ select_kernel(SelectArgs a) {
     const uint32_t base_bin =
         win ? (top_bin >= (uint32_t)(kSelBins - 1) ? top_bin - (kSelBins - 1) : 0u) : (top_bin >> width0) << width0;
 #pragma unroll
-    for (int j = 0; j < kKeysPerThread; ++j)
+    for (int j = 0; j < kKeys; ++j)
       if (key[j] != 0u && (key[j] >> shift0) >= base_bin) atomicAdd(&hist[(key[j] >> shift0) - base_bin], 1u);
     __syncthreads();
     if (wave == 0) {
@@ -624,13 +630,13 @@ select_kernel(SelectArgs a) {
       const unsigned long long lt = (1ull << lane) - 1ull;
       int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < kKeysPerThread; ++j) cnt += __popcll(__ballot(key[j] != 0u && key[j] >= lo_key));
+      for (int j = 0; j < kKeys; ++j) cnt += __popcll(__ballot(key[j] != 0u && key[j] >= lo_key));
       if (lane == 0) s_red[wave] = cnt;
       __syncthreads();
       int off = 0;
       for (int v = 0; v < wave; ++v) off += s_red[v];
 #pragma unroll
-      for (int j = 0; j < kKeysPerThread; ++j) {
+      for (int j = 0; j < kKeys; ++j) {
         const bool m = key[j] != 0u && key[j] >= lo_key;
         const unsigned long long bm = __ballot(m);
         if (m) {
@@ -743,7 +749,7 @@ select_kernel(SelectArgs a) {
           const int shift = top + 1 - width;
           const uint32_t dmask = (1u << width) - 1u;
   #pragma unroll
-          for (int j = 0; j < kKeysPerThread; ++j)
+          for (int j = 0; j < kKeys; ++j)
             if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
           __syncthreads();
           if (wave == 0) {
@@ -768,14 +774,14 @@ select_kernel(SelectArgs a) {
             const unsigned long long lt = (1ull << lane) - 1ull;
             int cnt = 0;
   #pragma unroll
-            for (int j = 0; j < kKeysPerThread; ++j)
+            for (int j = 0; j < kKeys; ++j)
               cnt += __popcll(__ballot(key[j] != 0u && (key[j] & mask) == prefix));
             if (lane == 0) s_red[wave] = cnt;
             __syncthreads();
             int off = 0;
             for (int v = 0; v < wave; ++v) off += s_red[v];
   #pragma unroll
-            for (int j = 0; j < kKeysPerThread; ++j) {
+            for (int j = 0; j < kKeys; ++j) {
               const bool m = key[j] != 0u && (key[j] & mask) == prefix;
               const unsigned long long bm = __ballot(m);
               if (m) s_lkey[off + __popcll(bm & lt)] = key[j];
@@ -827,7 +833,7 @@ select_kernel(SelectArgs a) {
     // counted with ballots; ties are taken lowest position first.
     uint32_t cgt = 0, ceq = 0;
   #pragma unroll
-    for (int j = 0; j < kKeysPerThread; ++j) {
+    for (int j = 0; j < kKeys; ++j) {
       cgt += key[j] > thr;
       ceq += (key[j] == thr) && (base + 64 * j < n);
     }
@@ -845,7 +851,7 @@ select_kernel(SelectArgs a) {
     }
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
   #pragma unroll
-    for (int j = 0; j < kKeysPerThread; ++j) {
+    for (int j = 0; j < kKeys; ++j) {
       const int i = base + 64 * j;
       const uint32_t k = key[j];
       const bool gt = k > thr;
@@ -895,10 +901,16 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int6
 hipError_t prepare_select() { return hipSuccess; }
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
-                         hipStream_t stream) {
+                         bool wide, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   dim3 grid((unsigned)n_chunks, (unsigned)n_rows);
   const bool ids = a.ids_in != nullptr;
+  if (wide) {
+    // one level over up to kSelectChunkWide keys per row (no carried ids)
+    if (!final_level || ids || n_chunks != 1) return hipErrorInvalidValue;
+    select_kernel<true, false, kSelectChunkWide / kSelThreads><<<grid, kSelThreads, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   if (final_level) {
     if (ids)
       select_kernel<true, true><<<grid, kSelThreads, 0, stream>>>(a);

@@ -64,10 +64,13 @@ struct SelectArgs {
 // Keys held by one selection work-group (32 per thread), and the largest pool
 // (in blocks) a selection maps through.
 constexpr int kSelectChunk = 16384;
+// Rows of up to this many keys (and no carried ids) are selected in one level
+// by a work-group holding 32 keys per thread.
+constexpr int kSelectChunkWide = 32768;
 constexpr int kMaxPoolBlocks = 4096;
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
-                         hipStream_t stream);
+                         bool wide, hipStream_t stream);
 hipError_t prepare_select();
 
 // ---------------------------------------------------------------- attention

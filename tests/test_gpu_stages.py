@@ -185,7 +185,8 @@ def test_index_full_block_mode(csa2, case):
             check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], "topk")
 
 
-@pytest.mark.parametrize("n_vis_rows", [[4096, 1000, 1], [20000, 16385, 300]])
+@pytest.mark.parametrize("n_vis_rows", [[4096, 1000, 1], [20000, 16385, 300], [32768, 32767, 16385],
+                                        [40000, 32769, 5]])
 def test_index_full_flat_mode(csa2, n_vis_rows):
     n = max(n_vis_rows)
     cache, ora = make_index_case(csa2, [n], n, seed=17)
