@@ -103,6 +103,8 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB buffer once with a plain device copy "
                          "(a known-size kernel for scaling hardware byte counters)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (tiny decode, prefill chunk, batch-32 128K decode)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step as HIP graphs instead of launching every kernel from Python")
     return ap.parse_args()
@@ -476,6 +478,20 @@ def decode_b32(steps, warmup):
     return out
 
 
+def tiny_decode(steps, warmup):
+    """The tiny decode workload: batch 1, 4,096 entries, one Full layer (append,
+    scan, 64 of 512 blocks, Top-512, attention + SWA).  Latency-bound: its
+    cache (1.46 MB) sits in the caches, so it is reported in microseconds."""
+    c = build(wid=0)
+    wall, scan_ms, per_layer = run_gpu(c, steps, warmup, True)
+    out = {"workload": c["wl"].name, "batch": c["B"], "context_entries": c["T"],
+           "us_per_step": round(wall * 1e6 / steps, 2),
+           "query_tokens_per_s": round(c["B"] / (wall / steps), 1),
+           "scan_us": round(scan_ms * 1e3, 2)}
+    del c
+    return out
+
+
 def copy_bandwidth():
     """A plain 1-GiB device-to-device copy on this GPU (read + write bytes / time)."""
     import torch
@@ -649,6 +665,9 @@ def main():
         line["attention_b256_h64"] = reuse_attention(20, 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, args.cpu_rows)
+    if not args.no_configs:
+        line["other_workloads"] = {"tiny_decode": tiny_decode(20, 3), "prefill_chunk": prefill_chunk(10, 2),
+                                   "decode_b32_128k": decode_b32(10, 2)}
     print(json.dumps(line), flush=True)
 
 
