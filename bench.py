@@ -48,22 +48,22 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "f5817f0d6864476d354cc5ca23aaeb1fb62419a2c7c2d5bb6ae29cba4846d3c6",
-    "fetch_kib": 278648.938, "fetch_scale": 524288 / 262166.625,
-    "write_kib": 4175.792, "write_scale": 524288 / 524288.0,
+    "sha256": "bb8b5d67121fe2b78a0b9b697a274389b9fff6c6880473385d6cd66088db8e95",
+    "fetch_kib": 278651.594, "fetch_scale": 524288 / 262166.875,
+    "write_kib": 4186.573, "write_scale": 524288 / 524288.0,
 }
 
 
 # The same two counters for the 64-head attention at batch 256 (bench.py
-# --attention-only: 23 launches; profiles/attn_h64_kernel_reuse_b256_hbm_counters.txt), scaled
-# by the same copy calibration.
+# --attention-only --copy-calibration 512: 23 launches), scaled by the copy
+# run first in the same process.
 ATTN64_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "1c9b02fb35b2d1d99b492618019a92426dff3f319962445d2713dcad4a562fd3",
-    "fetch_kib": 46186.266, "fetch_scale": 524288 / 262166.625,
-    "write_kib": 32833.394, "write_scale": 524288 / 524288.0,
+    "sha256": "4014372a0666b32e37b1ece9e948bb56d338a36fbd745bc7c475f8c9c9503e02",
+    "fetch_kib": 44595.997, "fetch_scale": 524288 / 262161.4375,
+    "write_kib": 32923.595, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -99,6 +99,9 @@ def parse():
     ap.add_argument("--attention-only", action="store_true",
                     help="run only the batch-256, 64-head attention measurement and print its object "
                          "(for profiling that kernel; not the benchmark line)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the encoder prefill chunk measurement and print its object "
+                         "(for profiling those kernels; not the benchmark line)")
     ap.add_argument("--ctx", type=int, default=None, help="override the context (testing only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the steps, copy a MIB-MiB buffer once with a plain device copy "
@@ -492,6 +495,41 @@ def tiny_decode(steps, warmup):
     return out
 
 
+def path_flops_per_query(T, wl):
+    """Useful flops of one decode query through this path's layer stack at T
+    visible entries: the Full-layer scan (2 x 8 x 128 per entry), the pool
+    re-score of the Full layer and of every Reindex layer (2 x 8 x 128 per
+    candidate, at most 8 x k_blocks candidates), and every layer's attention
+    (2 x 2 x heads x 512 per attended key: Top-K plus the SWA window)."""
+    cand = min(8 * wl.k_blk, T)
+    n_re = sum(1 for m in wl.layers if m == "reindex")
+    keys = min(wl.k_pos, T) + min(wl.swa, T)
+    return (2 * 8 * 128 * T + 2 * 8 * 128 * cand * (1 + n_re)
+            + len(wl.layers) * 2 * 2 * wl.heads * 512 * keys)
+
+
+def pages_figures(c):
+    """The pages' own figures (no hardware stated for any) beside what this
+    build's layout and launch plan give."""
+    csa2, wl = c["csa2"], c["wl"]
+    per_entry = c["cache"].nbytes // (c["B"] * c["T"])
+    split = csa2.csa2_attn_workspace_size(c["B"], c["H"], wl.k_pos, wl.swa) > 0
+    return {
+        "bytes_per_entry": {"this_build": per_entry, "pages": 356},
+        "bytes_per_token_at_2_5_entries": {"this_build": per_entry * 2.5, "pages": 890},
+        "kernels_per_reuse_layer_decode": {
+            "this_build": 2 if split else 1,
+            "pages": 11,
+            "note": "ours: sparse attention with the SWA branch fused (+ the split merge at this batch); "
+                    "the pages count the whole fused layer"},
+        "decode_flops_1m_over_4k": {
+            "this_build": round(path_flops_per_query(1 << 20, wl) / path_flops_per_query(4096, wl), 3),
+            "pages": 1.25,
+            "note": "ours: the CSA2 path alone (indexer scan, re-scores, attention of the 20-layer stack); "
+                    "the pages: the whole model"},
+    }
+
+
 def copy_bandwidth():
     """A plain 1-GiB device-to-device copy on this GPU (read + write bytes / time)."""
     import torch
@@ -620,6 +658,9 @@ def main():
     if args.attention_only:
         print(json.dumps(reuse_attention(args.steps, args.warmup)))
         return
+    if args.prefill_only:
+        print(json.dumps(prefill_chunk(args.steps, args.warmup)))
+        return
     t_build = time.perf_counter()
     c = build(args.ctx)
     t_build = time.perf_counter() - t_build
@@ -660,6 +701,7 @@ def main():
         "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
         "build_s": round(t_build, 1),
     }
+    line["pages_figures"] = pages_figures(c)
     line["hbm_copy_GBs"] = copy_bandwidth()
     if not args.no_attention_roofline:
         line["attention_b256_h64"] = reuse_attention(20, 3)
