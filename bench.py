@@ -495,6 +495,47 @@ def tiny_decode(steps, warmup):
     return out
 
 
+def multi_query_scan(c, q_per_seq=4, steps=20, warmup=3):
+    """The Full-layer scan of a multi-query decode step on the 1M-context cache:
+    each of the 8 sequences checks q_per_seq queries at once (draft tokens,
+    n_vis = T - q_per_seq + 1 .. T), so 8 x q_per_seq query rows, laid out
+    sequence by sequence, share each indexer key read.  Algorithmic bytes:
+    every visible key read once per sequence (68 B per entry) + one 4-B block
+    key per block of 8 per row."""
+    import torch
+
+    import workloads as W
+
+    csa2, T, B = c["csa2"], c["T"], c["B"]
+    R = B * q_per_seq
+    dev = "cuda"
+    seqs = torch.arange(B, dtype=torch.int32, device=dev).repeat_interleave(q_per_seq)
+    nvis = (torch.arange(q_per_seq, dtype=torch.int32, device=dev) + (T - q_per_seq + 1)).repeat(B)
+    q_idx = W.bf16_normal((R, 8, 128), W.seed_for(c["wl"].seed, W.T_QIDX, 99), device=dev)
+    w = W.uniform01((R, 8), W.seed_for(c["wl"].seed, W.T_W, 99), device=dev)
+    keys = csa2.block_keys_buffer(R, T)
+
+    def run():
+        csa2.csa2_index_scan(c["cache"], q_idx, w, seqs, nvis, T, keys)
+
+    for _ in range(warmup):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
+    byt = IK_BYTES * T * B + BLOCK_KEY_BYTES * ((T + 7) // 8) * R
+    achieved = byt / (us * 1e-6) / 1e9
+    return {"queries_per_sequence": q_per_seq, "rows": R, "avg_launch_us": round(us, 2),
+            "query_tokens_per_s": round(R / (us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": byt}}
+
+
 def path_flops_per_query(T, wl):
     """Useful flops of one decode query through this path's layer stack at T
     visible entries: the Full-layer scan (2 x 8 x 128 per entry), the pool
@@ -701,6 +742,7 @@ def main():
         "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
         "build_s": round(t_build, 1),
     }
+    line["multi_query_scan"] = multi_query_scan(c)
     line["pages_figures"] = pages_figures(c)
     line["hbm_copy_GBs"] = copy_bandwidth()
     if not args.no_attention_roofline:

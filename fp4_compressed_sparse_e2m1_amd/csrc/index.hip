@@ -44,9 +44,10 @@ namespace csa2 {
 namespace {
 
 constexpr int kScoreThreads = 256;
-// Flat scoring of at least this many rows shares each key tile among 8 rows.
-constexpr int kScoreRowsMin = 16;
-// Entries per work-group of the many-row flat scoring (32 tiles per wave).
+// Scoring of at least this many rows, at least two per sequence on average,
+// shares each key tile among 8 rows.
+constexpr int kScoreRowsMin = 8;
+// Entries per work-group of the many-row scoring (32 tiles per wave).
 constexpr int kScoreRowsChunk = 2048;
 
 // Entries per work-group: long contiguous runs for the scan, short ones for the
@@ -185,17 +186,22 @@ score_kernel(ScoreArgs a) {
     run(std::false_type{});
 }
 
-// Flat scoring of many query rows (prefill: consecutive query tokens of one
-// sequence).  A work-group takes kRows = 2 * RP consecutive rows and one chunk
-// of entries.  Each 16-entry tile is loaded and dequantised once and
-// multiplied against every pair of rows: MFMA rows 0..7 are the first row's 8
-// heads and rows 8..15 the second row's, so no matrix row is padding and the
-// key reads and conversions are shared by the work-group's rows.  Rows of one
-// work-group that belong to different sequences are scored one sequence at a
-// time (each pass covers the rows of one sequence).
-template <int RP>
+// Scoring of many query rows that share sequences: prefill (consecutive query
+// tokens of one sequence, flat mode) and multi-query decode (several queries of
+// one sequence, e.g. draft tokens checked together, block-max mode).  A
+// work-group takes kRows = 2 * RP consecutive rows and one chunk of entries.
+// Each 16-entry tile is loaded and dequantised once and multiplied against
+// every pair of rows: MFMA rows 0..7 are the first row's 8 heads and rows
+// 8..15 the second row's, so no matrix row is padding and the key reads and
+// conversions are shared by the work-group's rows of one sequence.  Rows of
+// one work-group that belong to different sequences are scored one sequence
+// at a time (each pass covers the rows of one sequence).  MODE: kScoreFlat
+// writes every visible entry's key, kScoreBlockMax the maximum key of each
+// block of 8 entries (over the row's visible entries).
+template <int RP, int MODE>
 __global__ void __launch_bounds__(kScoreThreads)
 score_rows_kernel(ScoreArgs a, int32_t n_rows) {
+  static_assert(MODE == kScoreFlat || MODE == kScoreBlockMax, "flat or block-max scoring");
   static_assert(RP % 2 == 0, "row pairs are combined two at a time");
   constexpr int kRows = 2 * RP;
   constexpr int kTilesPerWave = kScoreRowsChunk / (4 * 16);
@@ -326,7 +332,14 @@ score_rows_kernel(ScoreArgs a, int32_t n_rows) {
             const float x = odd ? pb : pa;
             const float y = odd ? pa : pb;
             const float score = x + swap_rows16(y);
-            if (e < wr_nv[p2]) out[p2][e] = score_key(score);
+            if (MODE == kScoreFlat) {
+              if (e < wr_nv[p2]) out[p2][e] = score_key(score);
+            } else {
+              // maximum over the visible entries of each block of 8 (lanes
+              // c .. c + 7 of a 16-lane row hold one block of one row)
+              const uint32_t key = umax8(e < wr_nv[p2] ? score_key(score) : 0u);
+              if ((c & 7) == 0 && e < wr_nv[p2]) out[p2][e >> 3] = key;
+            }
           }
         }
       };
@@ -883,10 +896,28 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int6
   const int chunk = mode == kScorePool ? kScorePoolChunk : kScoreChunk;
   const int64_t chunks = (slots + chunk - 1) / chunk;
   if (chunks == 0 || n_rows == 0) return hipSuccess;
-  if (mode == kScoreFlat && n_rows >= kScoreRowsMin && slots <= ((int64_t)1 << 30)) {
-    constexpr int kRP = 4;
-    dim3 grid((unsigned)((slots + kScoreRowsChunk - 1) / kScoreRowsChunk), (unsigned)((n_rows + 2 * kRP - 1) / (2 * kRP)));
-    score_rows_kernel<kRP><<<grid, kScoreThreads, 0, stream>>>(a, n_rows);
+  // Rows that share sequences (at least two rows per sequence on average)
+  // share each key tile: the many-row kernel.  Rows of distinct sequences run
+  // one per work-group.
+  if (mode != kScorePool && n_rows >= kScoreRowsMin && n_rows >= 2 * (int64_t)a.n_seq &&
+      slots <= ((int64_t)1 << 30)) {
+    // 8 rows per work-group; 4 when the sequences have at most 4 rows each on
+    // average (a few queries per sequence), so a work-group's rows are mostly
+    // one sequence's and no pass multiplies against rows it does not score
+    const int rp = n_rows <= 4 * (int64_t)a.n_seq ? 2 : 4;
+    dim3 grid((unsigned)((slots + kScoreRowsChunk - 1) / kScoreRowsChunk),
+              (unsigned)((n_rows + 2 * rp - 1) / (2 * rp)));
+    if (mode == kScoreFlat) {
+      if (rp == 2)
+        score_rows_kernel<2, kScoreFlat><<<grid, kScoreThreads, 0, stream>>>(a, n_rows);
+      else
+        score_rows_kernel<4, kScoreFlat><<<grid, kScoreThreads, 0, stream>>>(a, n_rows);
+    } else {
+      if (rp == 2)
+        score_rows_kernel<2, kScoreBlockMax><<<grid, kScoreThreads, 0, stream>>>(a, n_rows);
+      else
+        score_rows_kernel<4, kScoreBlockMax><<<grid, kScoreThreads, 0, stream>>>(a, n_rows);
+    }
     return hipGetLastError();
   }
   dim3 grid((unsigned)chunks, (unsigned)n_rows);

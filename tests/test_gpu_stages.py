@@ -229,6 +229,46 @@ def test_index_flat_many_rows(csa2):
         check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], f"row {r}")
 
 
+@pytest.mark.parametrize("per_seq", [3, 6])
+@pytest.mark.parametrize("k_blk", [300, 0])
+def test_index_multi_query_rows(csa2, per_seq, k_blk):
+    """Several query rows per sequence (multi-query decode: draft tokens whose
+    n_vis grow by one, checked together), in block mode (pool, then Top-K)
+    and flat mode: rows share key tiles in the many-row scoring kernel (4 rows
+    per work-group at 3 rows per sequence, 8 at 6).  Also an out-of-range
+    sequence id, an empty row, and rows of one sequence split across work-groups."""
+    n_list = [6000, 4100, 9001]
+    cache, ora = make_index_case(csa2, n_list, 9001, seed=51 + per_seq)
+    rows = []
+    for s, n in enumerate(n_list):
+        rows += [(s, n - per_seq + 1 + i) for i in range(per_seq)]
+    rows += [(5, 100), (1, 0), (2, 8193)]
+    R, k_pos = len(rows), 256
+    qidx = W.bf16_normal((R, 8, 128), seed=52)
+    w = W.uniform01((R, 8), seed=53)
+    pool, npool, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [s for s, _ in rows],
+                                        [n for _, n in rows], max(n for _, n in rows), k_blk, k_pos)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    for r, (s, nv) in enumerate(rows):
+        if s >= len(n_list) or nv == 0:
+            assert ntopk[r] == 0 and np.all(topk[r] == -1), r
+            if k_blk:
+                assert npool[r] == 0 and np.all(pool[r] == -1), r
+            continue
+        _, _, ikc, iks = ora[s]
+        ref = oracle.full_layer_select(qb[r], wn[r], ikc, iks, nv, k_blk, k_pos)
+        if k_blk == 0:
+            sc = ref["entry_scores"]
+            check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], f"flat row {r}")
+            continue
+        bs = ref["block_scores"]
+        check_selection(pool[r], npool[r], np.pad(ref["pool"], (0, k_blk - len(ref["pool"])),
+                        constant_values=-1), len(ref["pool"]), lambda b: bs[b], f"pool row {r}")
+        if np.array_equal(pool[r][:npool[r]], ref["pool"]):
+            sc = dict(zip(ref["cand"].tolist(), ref["cand_scores"].tolist()))
+            check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], f"topk row {r}")
+
+
 @pytest.mark.parametrize("kind", ["outlier", "tied_block", "narrow_spread"])
 def test_index_flat_selection_regimes(csa2, kind):
     """Score distributions that steer the selection off its common case:
