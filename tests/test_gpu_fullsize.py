@@ -144,6 +144,55 @@ def test_decode_b8_1m_full_reindex_reuse(csa2):
         np.testing.assert_array_equal(c["cache"].kv_scales[s, T - 1].cpu().numpy(), ks[0])
 
 
+# ------------------------------------------- multi-query decode at 1M context
+def test_multi_query_scan_1m(csa2):
+    """The multi-query scan as bench.py times it (8 sequences x 4 queries on
+    the 1M-entry cache, rows sequence by sequence, n_vis = T - 3 .. T), then
+    the pool and Top-512 of those rows; sampled rows against the oracle."""
+    import bench
+
+    c = bench.build()
+    bench._append(c)
+    wl, T, B = c["wl"], c["T"], c["B"]
+    q = 4
+    R = B * q
+    seqs = torch.arange(B, dtype=torch.int32, device="cuda").repeat_interleave(q)
+    nvis = (torch.arange(q, dtype=torch.int32, device="cuda") + (T - q + 1)).repeat(B)
+    q_idx = W.bf16_normal((R, 8, 128), W.seed_for(wl.seed, W.T_QIDX, 99), device="cuda")
+    w = W.uniform01((R, 8), W.seed_for(wl.seed, W.T_W, 99), device="cuda")
+    keys = csa2.block_keys_buffer(R, T)
+    csa2.csa2_index_scan(c["cache"], q_idx, w, seqs, nvis, T, keys)
+    pool = torch.empty((R, wl.k_blk), dtype=torch.int32, device="cuda")
+    npool = torch.empty(R, dtype=torch.int32, device="cuda")
+    topk = torch.empty((R, wl.k_pos), dtype=torch.int32, device="cuda")
+    ntopk = torch.empty(R, dtype=torch.int32, device="cuda")
+    ws = csa2.workspace(csa2.CSA2_OP_INDEX_POOL, R, T, wl.k_blk, wl.k_pos)
+    csa2.csa2_index_pool(c["cache"], q_idx, w, seqs, nvis, T, keys, wl.k_blk, wl.k_pos, pool, npool,
+                         topk, ntopk, ws)
+    torch.cuda.synchronize()
+    qi, wv = W.bf16_bits(q_idx), w.cpu().numpy()
+    pool_h, npool_h = pool.cpu().numpy(), npool.cpu().numpy()
+    topk_h, ntopk_h = topk.cpu().numpy(), ntopk.cpu().numpy()
+    nvis_h = nvis.cpu().numpy()
+    sample = {0: [1, 3], 5: [20, 22]}           # sequence -> rows (n_vis T - 2, T; T - 3, T - 1)
+
+    def ik_rows(s):
+        ik = W.rms_rows(T - 1, 128, W.seed_for(wl.seed, W.T_IKEY, 0, s), device="cuda")
+        return torch.cat([ik, c["new_ik"][s:s + 1]]).cpu().numpy()
+
+    planes = {s: oracle.quantize(ik_rows(s), oracle.IK_GROUP) for s in sample}
+    jobs = [(s, r) for s, rows in sample.items() for r in rows]
+    refs = oracle.parallel_map(
+        lambda sr: oracle.full_layer_select(qi[sr[1]], wv[sr[1]], *planes[sr[0]], int(nvis_h[sr[1]]),
+                                            wl.k_blk, wl.k_pos), jobs, len(jobs))
+    for (s, r), f in zip(jobs, refs):
+        bs = f["block_scores"]
+        check_selection(pool_h[r], npool_h[r], f["pool"], len(f["pool"]), lambda b: bs[b], f"pool row {r}")
+        if np.array_equal(pool_h[r][:npool_h[r]], f["pool"]):
+            sc = dict(zip(f["cand"].tolist(), f["cand_scores"].tolist()))
+            check_selection(topk_h[r], ntopk_h[r], f["topk"], f["n_topk"], lambda j: sc[j], f"topk row {r}")
+
+
 # ------------------------------------------------------ 128K decode, 18 Reindex
 def test_decode_b32_128k_full_18_reindex(csa2):
     wl = W.WORKLOADS[2]
