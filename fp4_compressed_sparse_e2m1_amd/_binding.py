@@ -58,6 +58,10 @@ def load():
         lib.csa2_quantize_fp4.restype = ctypes.c_int
         lib.csa2_cache_append.argtypes = [P, P, P, i64, P, P]
         lib.csa2_cache_append.restype = ctypes.c_int
+        lib.csa2_cache_export.argtypes = [P, i32, i64, i64, P, P]
+        lib.csa2_cache_export.restype = ctypes.c_int
+        lib.csa2_cache_import.argtypes = [P, i32, i64, i64, P, P]
+        lib.csa2_cache_import.restype = ctypes.c_int
         lib.csa2_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         lib.csa2_workspace_size.restype = sz
         lib.csa2_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
@@ -195,6 +199,30 @@ def csa2_cache_append(cache: Cache, latent, ikey, dst_rows, stream=None):
                                _ptr(ikey, torch.float32, "ikey", (n, 128)), n,
                                _ptr(dst_rows, torch.int64, "dst_rows", (n,)), _stream(stream))
     _check("csa2_cache_append", st)
+
+
+RECORD_BYTES = 356
+
+
+def csa2_cache_export(cache: Cache, seq: int, first: int, count: int, records, stream=None):
+    """Entries first .. first + count - 1 of sequence seq as count records of
+    356 bytes (uint8 device tensor [count, 356]; kv codes, kv scales, indexer
+    codes, indexer scales)."""
+    lib = load()
+    cs = cache.struct()
+    rp = _ptr(records, torch.uint8, "records", (count, RECORD_BYTES)) if count > 0 else None
+    _check("csa2_cache_export", lib.csa2_cache_export(ctypes.byref(cs), seq, first, count, rp,
+                                                      _stream(stream)))
+
+
+def csa2_cache_import(cache: Cache, seq: int, first: int, count: int, records, stream=None):
+    """Writes count records (uint8 device tensor [count, 356]) into entries
+    first .. first + count - 1 of sequence seq."""
+    lib = load()
+    cs = cache.struct()
+    rp = _ptr(records, torch.uint8, "records", (count, RECORD_BYTES)) if count > 0 else None
+    _check("csa2_cache_import", lib.csa2_cache_import(ctypes.byref(cs), seq, first, count, rp,
+                                                      _stream(stream)))
 
 
 def csa2_index_full(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, k_blocks, k_pos,

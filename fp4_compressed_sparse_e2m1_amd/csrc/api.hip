@@ -290,6 +290,23 @@ csa2_status attach_workspace(AttnArgs &a, int32_t n_rows, int32_t n_heads, int32
   return CSA2_OK;
 }
 
+// Shared checks and launch of csa2_cache_export / csa2_cache_import.
+csa2_status run_records(bool to_records, const csa2_cache *cache, int32_t seq, int64_t first,
+                        int64_t count, const uint8_t *records, void *stream) {
+  if (!cache_ok(cache, true, true)) return CSA2_E_INVALID_ARG;
+  if (!aligned(cache->kv_scales, 4) || !aligned(cache->ik_scales, 4)) return CSA2_E_INVALID_ARG;
+  if (seq < 0 || seq >= cache->n_seq || first < 0 || count < 0 || first > cache->cap ||
+      count > cache->cap - first)
+    return CSA2_E_INVALID_ARG;
+  if (count == 0) return CSA2_OK;
+  if (!records || !aligned(records, 4)) return CSA2_E_INVALID_ARG;
+  if (count > ((int64_t)1 << 32)) return CSA2_E_UNSUPPORTED;
+  hipError_t e = launch_records(to_records, cache->kv_codes, cache->kv_scales, cache->ik_codes,
+                                cache->ik_scales, (int64_t)seq * cache->cap + first, count,
+                                const_cast<uint8_t *>(records), reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -322,6 +339,16 @@ csa2_status csa2_cache_append(const csa2_cache *cache, const float *latent, cons
                                cache->ik_codes, cache->ik_scales, plane_rows,
                                reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
+csa2_status csa2_cache_export(const csa2_cache *cache, int32_t seq, int64_t first, int64_t count,
+                              uint8_t *records, void *stream) {
+  return run_records(true, cache, seq, first, count, records, stream);
+}
+
+csa2_status csa2_cache_import(const csa2_cache *cache, int32_t seq, int64_t first, int64_t count,
+                              const uint8_t *records, void *stream) {
+  return run_records(false, cache, seq, first, count, records, stream);
 }
 
 size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,

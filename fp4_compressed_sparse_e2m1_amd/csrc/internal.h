@@ -131,4 +131,13 @@ hipError_t launch_append(const float *lat, const float *ik, int64_t n, const int
                          uint8_t *kv_codes, uint8_t *kv_scales, uint8_t *ik_codes, uint8_t *ik_scales,
                          int64_t plane_rows, hipStream_t stream);
 
+// ---------------------------------------------------------- cache records
+// Entry records of 356 bytes (the four planes' bytes of one entry, in plane
+// order) for entries [first, first + count) of one sequence; `plane_row0` is
+// the plane row of the first entry.  export: planes -> records; import:
+// records -> planes.
+hipError_t launch_records(bool to_records, uint8_t *kv_codes, uint8_t *kv_scales, uint8_t *ik_codes,
+                          uint8_t *ik_scales, int64_t plane_row0, int64_t count, uint8_t *records,
+                          hipStream_t stream);
+
 }  // namespace csa2

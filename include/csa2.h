@@ -140,6 +140,29 @@ csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t gr
 csa2_status csa2_cache_append(const csa2_cache *cache, const float *latent, const float *ikey,
                               int64_t n, const int64_t *dst_rows, void *stream);
 
+/* Cache records -- export and import of stored entries, byte for byte
+ * [P3 "레이어 40개 가운데 4개만 전역 캐시를 만듭니다": a stored entry is
+ * 356 B (the 288-B latent and the 68-B indexer key), 890 B per token at 2.5
+ * entries; the pages keep such caches beyond the GPU for later reuse].
+ * A record is one entry's 356 bytes in the order of the planes:
+ *   [0, 256)   kv_codes   [256, 288) kv_scales
+ *   [288, 352) ik_codes   [352, 356) ik_scales
+ * and entries first .. first + count - 1 of sequence seq form count
+ * consecutive records (count * 356 bytes) in `records`, a DEVICE buffer
+ * owned by the caller (copy it to or from host memory with the caller's own
+ * stream).  csa2_cache_export writes the records from the cache's planes;
+ * csa2_cache_import writes the planes from the records (the entries' previous
+ * bytes are replaced).  Both are plain byte copies: an exported and
+ * re-imported range is bit-identical.
+ * Requires a cache with all four planes (each 4-B aligned), 0 <= seq < n_seq,
+ * first >= 0, count >= 0, first + count <= cap, and a 4-B aligned `records`
+ * (may be NULL when count = 0). */
+#define CSA2_RECORD_BYTES 356
+csa2_status csa2_cache_export(const csa2_cache *cache, int32_t seq, int64_t first, int64_t count,
+                              uint8_t *records, void *stream);
+csa2_status csa2_cache_import(const csa2_cache *cache, int32_t seq, int64_t first, int64_t count,
+                              const uint8_t *records, void *stream);
+
 /* Scratch bytes that csa2_index_full (op CSA2_OP_INDEX_FULL),
  * csa2_index_reindex (op CSA2_OP_INDEX_REINDEX) or csa2_index_pool (op
  * CSA2_OP_INDEX_POOL) needs for these sizes; k_blocks = 0 selects flat mode

@@ -181,3 +181,22 @@ def test_binding_rejects_host_tensors():
     scales = torch.zeros(4, 32, dtype=torch.uint8)
     with pytest.raises(ValueError):
         csa2.csa2_quantize_fp4(x, 16, codes, scales)
+
+
+def test_cache_record_validation():
+    """Export / import reject bad ranges and buffers before any launch; an
+    empty range is a no-op."""
+    lib = csa2.load()
+    for f in (lib.csa2_cache_export, lib.csa2_cache_import):
+        cs = cache_struct(cap=100, n_seq=2)
+        assert f(ctypes.byref(cs), 0, 0, 0, None, None) == OK            # nothing to copy
+        assert f(ctypes.byref(cs), 2, 0, 1, FAKE, None) == INVALID       # sequence out of range
+        assert f(ctypes.byref(cs), -1, 0, 1, FAKE, None) == INVALID
+        assert f(ctypes.byref(cs), 0, -1, 1, FAKE, None) == INVALID      # negative first
+        assert f(ctypes.byref(cs), 0, 90, 11, FAKE, None) == INVALID     # past cap
+        assert f(ctypes.byref(cs), 0, 101, 0, FAKE, None) == INVALID
+        assert f(ctypes.byref(cs), 0, 0, -1, FAKE, None) == INVALID
+        assert f(ctypes.byref(cs), 0, 0, 5, None, None) == INVALID       # no buffer
+        assert f(ctypes.byref(cs), 0, 0, 5, FAKE + 2, None) == INVALID   # misaligned buffer
+        assert f(ctypes.byref(cache_struct(null_ik=True)), 0, 0, 5, FAKE, None) == INVALID
+        assert f(None, 0, 0, 5, FAKE, None) == INVALID

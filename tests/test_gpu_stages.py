@@ -125,6 +125,38 @@ def test_cache_append_both_planes(csa2):
         assert not got[untouched].any()
 
 
+def test_cache_records_export_import(csa2):
+    """Entry records (356 B: kv codes, kv scales, indexer codes, indexer
+    scales) equal the oracle's encoding of the same rows laid out in that
+    order, and a range exported from one cache and imported into another
+    (different sequence and offset) reproduces the planes byte for byte
+    without touching the entries around it."""
+    n, cap = 1000, 1200
+    lat = W.rms_rows(n, 512, seed=61).numpy()
+    ik = W.rms_rows(n, 128, seed=62).numpy()
+    src = csa2.Cache(2, cap)
+    dst_rows = torch.arange(n, dtype=torch.int64, device="cuda") + cap + 100      # sequence 1, from 100
+    csa2.csa2_cache_append(src, dev(lat), dev(ik), dst_rows)
+    first, count = 137, 777
+    rec = torch.full((count, 356), 0xAB, dtype=torch.uint8, device="cuda")
+    csa2.csa2_cache_export(src, 1, 100 + first, count, rec)
+    kvc, kvs = oracle.quantize(lat[first:first + count], 16)
+    ikc, iks = oracle.quantize(ik[first:first + count], 32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(rec.cpu().numpy(), np.concatenate([kvc, kvs, ikc, iks], axis=1))
+    dst = csa2.Cache(3, 900)
+    for plane in (dst.kv_codes, dst.kv_scales, dst.ik_codes, dst.ik_scales):
+        plane.fill_(0x5A)
+    csa2.csa2_cache_import(dst, 2, 900 - count, count, rec)
+    csa2.csa2_cache_export(dst, 2, 0, 0, None)                                  # empty range: no-op
+    torch.cuda.synchronize()
+    for a, b in ((dst.kv_codes, src.kv_codes), (dst.kv_scales, src.kv_scales),
+                 (dst.ik_codes, src.ik_codes), (dst.ik_scales, src.ik_scales)):
+        np.testing.assert_array_equal(a[2, 900 - count:].cpu().numpy(),
+                                      b[1, 100 + first:100 + first + count].cpu().numpy())
+        assert torch.all(a[2, :900 - count] == 0x5A) and torch.all(a[:2] == 0x5A)
+
+
 # ------------------------------------------------------------- S2-S4 index
 def make_index_case(csa2, n_list, cap, seed, k_rows=None):
     lat = [W.rms_rows(n, 512, seed=seed + 10 * i).numpy() for i, n in enumerate(n_list)]
