@@ -48,9 +48,9 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "bb8b5d67121fe2b78a0b9b697a274389b9fff6c6880473385d6cd66088db8e95",
-    "fetch_kib": 278651.594, "fetch_scale": 524288 / 262166.875,
-    "write_kib": 4186.573, "write_scale": 524288 / 524288.0,
+    "sha256": "27e907e882c97fbe8e1f19949ea8426ef8c15d3fb75fc1eac3767f923edb9751",
+    "fetch_kib": 278653.406, "fetch_scale": 524288 / 262165.375,
+    "write_kib": 4177.703, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -61,9 +61,9 @@ ATTN64_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "4014372a0666b32e37b1ece9e948bb56d338a36fbd745bc7c475f8c9c9503e02",
-    "fetch_kib": 44595.997, "fetch_scale": 524288 / 262161.4375,
-    "write_kib": 32923.595, "write_scale": 524288 / 524288.0,
+    "sha256": "8a63e0c5e189c6be919c9028678285997c3a720984a736a968e2e50247145ac3",
+    "fetch_kib": 44253.595, "fetch_scale": 524288 / 262161.875,
+    "write_kib": 32919.541, "write_scale": 524288 / 524288.0,
 }
 
 
