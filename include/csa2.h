@@ -191,6 +191,11 @@ size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t
  *   n_topk[r] the count.
  * Types: q_idx bf16 bits [n_rows][8][128]; w fp32 [n_rows][8]; row_seq,
  * row_nvis int32 [n_rows]; outputs int32.
+ * Several rows may name the same sequence (prefill query tokens, or several
+ * decode queries of one sequence checked together); when the rows are at
+ * least twice the cache's sequences, the scoring reads each indexer key once
+ * for up to 8 consecutive rows of one sequence, so such rows are best laid
+ * out sequence by sequence.  Results do not depend on the layout.
  * Requires 1 <= n_rows, 0 <= max_nvis <= cap, max_nvis < 2^31 - 8,
  * 0 <= k_blocks <= 4096, 1 <= k_pos <= 4096, and workspace_bytes >=
  * csa2_workspace_size(CSA2_OP_INDEX_FULL, n_rows, max_nvis, k_blocks, k_pos). */
