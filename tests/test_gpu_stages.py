@@ -218,7 +218,7 @@ def test_index_full_block_mode(csa2, case):
 
 
 @pytest.mark.parametrize("n_vis_rows", [[4096, 1000, 1], [20000, 16385, 300], [32768, 32767, 16385],
-                                        [40000, 32769, 5]])
+                                        [40000, 32769, 5], [140001, 70000]])
 def test_index_full_flat_mode(csa2, n_vis_rows):
     n = max(n_vis_rows)
     cache, ora = make_index_case(csa2, [n], n, seed=17)
