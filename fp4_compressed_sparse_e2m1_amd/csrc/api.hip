@@ -419,7 +419,7 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   if (!cache_ok(cache, true, false)) return CSA2_E_INVALID_ARG;
   if (!q || !row_seq || !topk || !n_topk || !o || !lse) return CSA2_E_INVALID_ARG;
   if (n_rows < 0 || k_pos < 1 || !isfinite(scale)) return CSA2_E_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(o, 4) || !aligned(lse, 4)) return CSA2_E_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4)) return CSA2_E_INVALID_ARG;
   if (n_heads != 16 && n_heads != 32 && n_heads != 64) return CSA2_E_UNSUPPORTED;
   if (k_pos > kMaxAttnPos) return CSA2_E_UNSUPPORTED;
   if (swa && !swa_ok(swa)) return CSA2_E_INVALID_ARG;
@@ -458,7 +458,7 @@ csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *ro
                            void *stream) {
   if (!q || !row_seq || !o || !lse || !swa_ok(swa)) return CSA2_E_INVALID_ARG;
   if (n_rows < 0 || n_seq < 1 || !isfinite(scale)) return CSA2_E_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(o, 4) || !aligned(lse, 4)) return CSA2_E_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4)) return CSA2_E_INVALID_ARG;
   if (n_heads != 16 && n_heads != 32 && n_heads != 64) return CSA2_E_UNSUPPORTED;
   if (n_rows == 0) return CSA2_OK;
   AttnArgs a = {};

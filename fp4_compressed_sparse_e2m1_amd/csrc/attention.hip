@@ -53,8 +53,10 @@ struct KeySwa {
 //     otherwise).  Probabilities enter P.V in f16 and the normaliser sums the
 //     same rounded values.
 //   * P.V: the waves' P rows and dequantised keys go to LDS; wave w then
-//     accumulates O[:, 128w .. 128w + 127] over all 64 keys of the tile, the V
-//     operand read back with the hardware transposed LDS read.
+//     accumulates channels 128w .. 128w + 127 of O over all 64 keys of the
+//     tile, the V operand read back with the hardware transposed LDS read; as
+//     O^T = V^T P^T (each lane ends with four consecutive channels of one
+//     head, stored with 16-B writes) when a row is not split, else as O = P V.
 // Two work-group barriers per 64 keys.  A 32- or 64-head layer runs 2 or 4
 // head groups per row, given block ids that put them on one XCD, so the keys
 // they all gather come from its L2.
@@ -62,6 +64,10 @@ constexpr int kKsHeads = 16;
 constexpr int kKsVStride = 512 + 8;    // halves per LDS key row (16-B writes of 16 rows on distinct banks)
 constexpr int kKsPStride = 64 + 8;     // halves per LDS P row
 
+// OT: the O accumulators hold O^T (four consecutive channels of one head per
+// lane, 16-B stores; used when rows are not split), else O (four heads of one
+// channel per lane; measured faster for the split partials of small batches).
+template <bool OT>
 __global__ void __launch_bounds__(kAttnThreads)
 attn_kernel(AttnArgs a) {
   constexpr int H = kKsHeads;
@@ -128,18 +134,30 @@ attn_kernel(AttnArgs a) {
     for (int t = 0; t < 16; ++t) qa[t] = bf16x8_to_f16(qp[t]);
   }
 
-  // O[:, 128w + 16db + c] for heads 4G .. 4G + 3 (lane (G, c), element i)
+  // Accumulators, lane (G, c), block db: OT: O[head h0 + c][channels
+  // 128w + 16db + 4G .. +3] (four consecutive channels of one head, stored
+  // with one 16-B access); else element i: O[head h0 + 4G + i][channel
+  // 128w + 16db + c]
   f32x4 acc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (merge_in) {
+    if (OT) {
+      const int64_t hrow = (int64_t)r * HT + h0 + c;
+      if (a.lse[hrow] != -INFINITY) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = h0 + 4 * G + i;
-      const float lin = a.lse[(int64_t)r * HT + h];
-      if (lin != -INFINITY) {
+        for (int db = 0; db < 8; ++db)
+          acc[db] = *reinterpret_cast<const f32x4 *>(a.o + hrow * 512 + 128 * w + 16 * db + 4 * G);
+      }
+    } else {
 #pragma unroll
-        for (int db = 0; db < 8; ++db) acc[db][i] = a.o[((int64_t)r * HT + h) * 512 + 128 * w + 16 * db + c];
+      for (int i = 0; i < 4; ++i) {
+        const int h = h0 + 4 * G + i;
+        const float lin = a.lse[(int64_t)r * HT + h];
+        if (lin != -INFINITY) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) acc[db][i] = a.o[((int64_t)r * HT + h) * 512 + 128 * w + 16 * db + c];
+        }
       }
     }
   }
@@ -262,23 +280,31 @@ attn_kernel(AttnArgs a) {
       *reinterpret_cast<f16x8 *>(&s_v[(16 * w + c) * kKsVStride + 128 * G + 8 * t]) = kf[t];
     *reinterpret_cast<f16x4 *>(&s_p[c * kKsPStride + 16 * w + 4 * G]) = f16x4{ph[0], ph[1], ph[2], ph[3]};
     __syncthreads();
-    // O[:, quarter w] = alpha * O + P V over the tile's 64 keys (the rescale
-    // is skipped while the running maxima of these heads stand still)
-    const float4 al = *reinterpret_cast<const float4 *>(&s_alpha[4 * G]);
-    if (__builtin_amdgcn_ballot_w64(al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f)) {
+    // O^T[quarter w, :] = alpha * O^T + V^T P^T over the tile's 64 keys (the
+    // rescale is skipped while the running maxima of these heads stand still)
+    if (OT) {
+      const float al = s_alpha[c];
+      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        acc[db][0] *= al.x;
-        acc[db][1] *= al.y;
-        acc[db][2] *= al.z;
-        acc[db][3] *= al.w;
+        for (int db = 0; db < 8; ++db) acc[db] *= al;
+      }
+    } else {
+      const float4 al = *reinterpret_cast<const float4 *>(&s_alpha[4 * G]);
+      if (__builtin_amdgcn_ballot_w64(al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          acc[db][0] *= al.x;
+          acc[db][1] *= al.y;
+          acc[db][2] *= al.z;
+          acc[db][3] *= al.w;
+        }
       }
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      // A: P[head c][keys 32kk + 8G .. +7]; B: V[keys 32kk + 8G .. +7][channel
-      // 128w + 16db + c], from rows 32kk + 8G + 4h + c/4 (h = 0, 1) read
-      // transposed
+      // P[head c][keys 32kk + 8G .. +7] and V[keys 32kk + 8G .. +7][channel
+      // 128w + 16db + c] (rows 32kk + 8G + 4h + c/4, h = 0, 1, read
+      // transposed): O^T += V^T P^T (OT) or O += P V
       const f16x8 pa = *reinterpret_cast<const f16x8 *>(&s_p[c * kKsPStride + 32 * kk + 8 * G]);
       const _Float16 *r0 = &s_v[(32 * kk + 8 * G + (c >> 2)) * kKsVStride + 128 * w + 4 * (c & 3)];
       const _Float16 *r1 = r0 + 4 * kKsVStride;
@@ -292,7 +318,8 @@ attn_kernel(AttnArgs a) {
           vb[u] = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[db + u] = mfma16x16x32(pa, vb[u], acc[db + u]);
+        for (int u = 0; u < 2; ++u)
+          acc[db + u] = OT ? mfma16x16x32(vb[u], pa, acc[db + u]) : mfma16x16x32(pa, vb[u], acc[db + u]);
       }
     }
     // (the next tile writes LDS only after its first barrier, which every
@@ -346,12 +373,17 @@ attn_kernel(AttnArgs a) {
   if (split) {
     // unnormalised partial: O, running max (log2 units) and sum per head
     const int64_t part = (int64_t)r * a.n_split + sp;
+    if (OT) {
+      float *prow = a.part_o + (part * HT + h0 + c) * 512 + 128 * w + 4 * G;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * G + i;
-      float *prow = a.part_o + (part * HT + h0 + h) * 512 + 128 * w + c;
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(prow + 16 * db) = acc[db];
+    } else {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) prow[16 * db] = acc[db][i];
+      for (int i = 0; i < 4; ++i) {
+        float *prow = a.part_o + (part * HT + h0 + 4 * G + i) * 512 + 128 * w + c;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) prow[16 * db] = acc[db][i];
+      }
     }
     if (tid < H) {
       a.part_ml[(part * HT + h0 + tid) * 2] = s_m[tid];
@@ -360,14 +392,22 @@ attn_kernel(AttnArgs a) {
     return;
   }
   // normalise and store
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * G + i;
-    const float l = s_l[h];
+  if (OT) {
+    const float l = s_l[c];
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float *orow = a.o + ((int64_t)r * HT + h0 + h) * 512 + 128 * w + c;
+    float *orow = a.o + ((int64_t)r * HT + h0 + c) * 512 + 128 * w + 4 * G;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) orow[16 * db] = acc[db][i] * inv;
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(orow + 16 * db) = acc[db] * inv;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * G + i;
+      const float l = s_l[h];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float *orow = a.o + ((int64_t)r * HT + h0 + h) * 512 + 128 * w + c;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) orow[16 * db] = acc[db][i] * inv;
+    }
   }
   if (tid < H) {
     const float l = s_l[tid];
@@ -521,7 +561,10 @@ hipError_t launch_attention(const AttnArgs &args, int32_t n_heads, int32_t n_row
   if (n_heads == 64) {
     e = launch_attention_h64(a, blocks, stream);
   } else {
-    attn_kernel<<<dim3((unsigned)blocks), kAttnThreads, 0, stream>>>(a);
+    if (a.n_split > 1)
+      attn_kernel<false><<<dim3((unsigned)blocks), kAttnThreads, 0, stream>>>(a);
+    else
+      attn_kernel<true><<<dim3((unsigned)blocks), kAttnThreads, 0, stream>>>(a);
     e = hipGetLastError();
   }
   if (e != hipSuccess || a.n_split <= 1) return e;

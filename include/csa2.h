@@ -263,7 +263,7 @@ csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, c
  * csa2_swa_merge).  With no keys at all, o = 0 and lse = -inf.
  * Types: q bf16 bits [n_rows][n_heads][512]; topk int32 [n_rows][k_pos];
  * n_topk int32 [n_rows]; o fp32 [n_rows][n_heads][512]; lse fp32
- * [n_rows][n_heads].  Requires n_heads in {16, 32, 64}, n_rows >= 0,
+ * [n_rows][n_heads]; q and o 16-B aligned.  Requires n_heads in {16, 32, 64}, n_rows >= 0,
  * 1 <= k_pos <= 65536, scale finite.
  * workspace (optional, 256-B aligned, csa2_attn_workspace_size bytes): with
  * it, a small batch spreads each row's keys over several work-groups and

@@ -148,6 +148,7 @@ def test_attention_validation():
     assert call(7, 0) == INVALID                          # k_pos
     assert call(8, float("inf")) == INVALID               # scale
     assert call(1, FAKE + 2) == INVALID                   # misaligned q
+    assert call(10, FAKE + 4) == INVALID                  # o not 16-B aligned (vector stores)
     assert call(5, None) == INVALID                       # topk
     assert call(4, -1) == INVALID
     bad_swa = B._SwaStruct(FAKE, 128, FAKE, 2048)         # window too long
@@ -158,6 +159,7 @@ def test_attention_validation():
     assert m(FAKE, 16, FAKE, 4, ctypes.byref(good_swa), 0, 0.04, FAKE, FAKE, None, 0, None) == INVALID
     assert m(FAKE, 20, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == UNSUPPORTED
     assert m(FAKE, 16, FAKE, 0, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == OK
+    assert m(FAKE, 16, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE + 8, FAKE, None, 0, None) == INVALID
     # a split needs its workspace: given but too small is an error, NULL is not
     ws = lib.csa2_attn_workspace_size(8, 64, 512, 128)
     assert ws >= 8 * 2 * 64 * 514 * 4
