@@ -48,7 +48,7 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "27e907e882c97fbe8e1f19949ea8426ef8c15d3fb75fc1eac3767f923edb9751",
+    "sha256": "70cb37f403b3f23687f45a1673605c387fed9211bcbeb4e08870765e8f548161",
     "fetch_kib": 278653.406, "fetch_scale": 524288 / 262165.375,
     "write_kib": 4177.703, "write_scale": 524288 / 524288.0,
 }

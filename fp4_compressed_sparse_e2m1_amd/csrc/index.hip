@@ -10,6 +10,8 @@
 // One wave scores 16 entries per step with four 16x16x32 f16 MFMAs:
 //   rows (M) = 16 query heads (8 real, 8 zero), columns (N) = 16 entries,
 //   contraction (K) = 128 key channels in 4 steps of 32.
+// (Rows that share a sequence are scored in pairs instead -- MFMA rows = two
+// queries' 8 heads -- by score_rows_kernel below.)
 // Lane (G = lane/16, c = lane%16) loads 16 contiguous bytes of entry c's code
 // row -- channels [32G, 32G+32), exactly one scale group -- so the wave reads
 // a 1 KiB contiguous tile with one 16-byte load per lane.  MFMA step t uses
@@ -23,7 +25,8 @@
 //
 // Selection: scores are mapped to order-preserving uint32 keys (0 = no
 // candidate).  A 1,024-thread work-group holds up to 16,384 keys of one row in
-// registers (16 per thread).  One LDS histogram of up to 4,096 bins over the
+// registers (16 per thread; 32 per thread for rows of up to 32,768 keys that
+// are selected in one level).  One LDS histogram of up to 4,096 bins over the
 // first digit -- a window ending at the largest key, or the plain digit below
 // the highest bit in which the keys differ -- names the bin holding the k-th
 // key; the keys at or above that bin are gathered, in position order with
