@@ -549,9 +549,10 @@ def path_flops_per_query(T, wl):
             + len(wl.layers) * 2 * 2 * wl.heads * 512 * keys)
 
 
-def pages_figures(c):
+def pages_figures(c, step_ms_1m=None, step_ms_4k=None):
     """The pages' own figures (no hardware stated for any) beside what this
-    build's layout and launch plan give."""
+    build's layout and launch plan give, and the measured step-time ratio of
+    the same 20-layer decode stack at 1M and at 4K context when given."""
     csa2, wl = c["csa2"], c["wl"]
     per_entry = c["cache"].nbytes // (c["B"] * c["T"])
     split = csa2.csa2_attn_workspace_size(c["B"], c["H"], wl.k_pos, wl.swa) > 0
@@ -563,11 +564,19 @@ def pages_figures(c):
             "pages": 11,
             "note": "ours: sparse attention with the SWA branch fused (+ the split merge at this batch); "
                     "the pages count the whole fused layer"},
+        "kernels_per_reuse_layer_prefill": {
+            "this_build": 1 if csa2.csa2_attn_workspace_size(4096, c["H"], wl.k_pos, wl.swa) == 0 else 2,
+            "pages": 15,
+            "note": "ours at the 4,096-query prefill chunk: one attention launch with the SWA branch fused"},
         "decode_flops_1m_over_4k": {
             "this_build": round(path_flops_per_query(1 << 20, wl) / path_flops_per_query(4096, wl), 3),
             "pages": 1.25,
             "note": "ours: the CSA2 path alone (indexer scan, re-scores, attention of the 20-layer stack); "
                     "the pages: the whole model"},
+        "decode_step_time_1m_over_4k": {
+            "this_build": round(step_ms_1m / step_ms_4k, 3) if step_ms_1m and step_ms_4k else None,
+            "ms_at_4k": round(step_ms_4k, 4) if step_ms_4k else None,
+            "note": "measured: the same 20-layer decode step (batch 8) at 4,096 and at 1,048,576 entries"},
     }
 
 
@@ -743,7 +752,10 @@ def main():
         "build_s": round(t_build, 1),
     }
     line["multi_query_scan"] = multi_query_scan(c)
-    line["pages_figures"] = pages_figures(c)
+    c4k = build(4096)
+    wall4k, _, _ = run_gpu(c4k, args.steps, args.warmup, True)
+    del c4k
+    line["pages_figures"] = pages_figures(c, ms_step, wall4k * 1e3 / args.steps)
     line["hbm_copy_GBs"] = copy_bandwidth()
     if not args.no_attention_roofline:
         line["attention_b256_h64"] = reuse_attention(20, 3)
