@@ -380,6 +380,33 @@ def test_index_reindex_on_oracle_pool(csa2):
                         lambda j: sc[j], "reindex-flat")
 
 
+def test_index_reindex_flat_many_rows(csa2):
+    """Prefill Reindex: flat re-scoring of all visible entries for many query
+    rows of a few sequences (no pool: the encoder keeps none), the rows of a
+    sequence sharing key tiles in the many-row kernel."""
+    n_list = [7000, 2500]
+    cache, ora = make_index_case(csa2, n_list, 7000, seed=81)
+    rows = [(0, 6980 + i) for i in range(20)] + [(1, 2490 + i) for i in range(11)] + [(0, 5), (1, 0)]
+    R, k_pos = len(rows), 384
+    q_re = W.bf16_normal((R, 8, 128), seed=82)
+    w_re = W.uniform01((R, 8), seed=83)
+    max_nvis = max(n for _, n in rows)
+    ws = csa2.workspace(csa2.CSA2_OP_INDEX_REINDEX, R, max_nvis, 0, k_pos)
+    topk = torch.full((R, k_pos), -7, dtype=torch.int32, device="cuda")
+    ntopk = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    csa2.csa2_index_reindex(cache, dev(q_re), dev(w_re), dev([s for s, _ in rows], torch.int32),
+                            dev([n for _, n in rows], torch.int32), max_nvis, None, None, 0, k_pos,
+                            topk, ntopk, ws)
+    torch.cuda.synchronize()
+    topk, ntopk = topk.cpu().numpy(), ntopk.cpu().numpy()
+    qb, wn = W.bf16_bits(q_re), w_re.numpy()
+    for r, (s, nv) in enumerate(rows):
+        _, _, ikc, iks = ora[s]
+        ref = oracle.reindex_select(qb[r], wn[r], ikc, iks, nv, None, k_pos)
+        sc = ref["cand_scores"]
+        check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], f"row {r}")
+
+
 # ------------------------------------------------------------ S5-S6 attention
 def attn_case(csa2, H, n_vis_list, topk_rows, swa_ends, seed=0, swa_len=200, window=128):
     S = len(n_vis_list)
