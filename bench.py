@@ -752,6 +752,11 @@ def main():
         "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
         "build_s": round(t_build, 1),
     }
+    if not args.graph and not args.no_configs:
+        # the same step replayed as three HIP graphs (checked bit for bit
+        # against the eager step first): the launch cost is the GPU's, not the host's
+        wall_g, _, _ = run_gpu(c, args.steps, args.warmup, False)
+        line["graph_replay_ms_per_step"] = round(wall_g * 1e3 / args.steps, 4)
     line["multi_query_scan"] = multi_query_scan(c)
     ms_4k = None
     if not args.no_configs:             # the same stack at 4,096 entries, for the 4K -> 1M ratio
