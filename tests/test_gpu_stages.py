@@ -261,19 +261,24 @@ def test_index_flat_many_rows(csa2):
         check_selection(topk[r], ntopk[r], ref["topk"], ref["n_topk"], lambda j: sc[j], f"row {r}")
 
 
+@pytest.mark.parametrize("interleave", [False, True])
 @pytest.mark.parametrize("per_seq", [3, 6])
 @pytest.mark.parametrize("k_blk", [300, 0])
-def test_index_multi_query_rows(csa2, per_seq, k_blk):
+def test_index_multi_query_rows(csa2, per_seq, k_blk, interleave):
     """Several query rows per sequence (multi-query decode: draft tokens whose
     n_vis grow by one, checked together), in block mode (pool, then Top-K)
     and flat mode: rows share key tiles in the many-row scoring kernel (4 rows
-    per work-group at 3 rows per sequence, 8 at 6).  Also an out-of-range
-    sequence id, an empty row, and rows of one sequence split across work-groups."""
+    per work-group at 3 rows per sequence, 8 at 6), laid out sequence by
+    sequence or interleaved (each work-group then scores several sequences in
+    turn).  Also an out-of-range sequence id, an empty row, and rows of one
+    sequence split across work-groups."""
     n_list = [6000, 4100, 9001]
     cache, ora = make_index_case(csa2, n_list, 9001, seed=51 + per_seq)
     rows = []
     for s, n in enumerate(n_list):
         rows += [(s, n - per_seq + 1 + i) for i in range(per_seq)]
+    if interleave:              # sequences alternate row by row: several passes per work-group
+        rows = [rows[per_seq * (i % 3) + i // 3] for i in range(len(rows))]
     rows += [(5, 100), (1, 0), (2, 8193)]
     R, k_pos = len(rows), 256
     qidx = W.bf16_normal((R, 8, 128), seed=52)
