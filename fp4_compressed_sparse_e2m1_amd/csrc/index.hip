@@ -135,8 +135,17 @@ score_kernel(ScoreArgs a) {
         if (FULL) {
           const int64_t d = ILV ? ((int64_t)(tb + u) * 4) * 16 : (int64_t)(tb + u) * 16;
           valid[u] = true;
-          craw[u] = *reinterpret_cast<const uint4 *>(cbase + d * 64);
-          sraw[u] = sbase[d * 4];
+          if (MODE == kScoreBlockMax) {
+            // The scan reads every key once: non-temporal loads keep its
+            // stream from evicting what the later layers reuse from L2 and the
+            // Infinity Cache (pool keys, gathered latents, SWA rows).
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cbase + d * 64));
+            craw[u] = uint4{v[0], v[1], v[2], v[3]};
+            sraw[u] = __builtin_nontemporal_load(sbase + d * 4);
+          } else {
+            craw[u] = *reinterpret_cast<const uint4 *>(cbase + d * 64);
+            sraw[u] = sbase[d * 4];
+          }
           continue;
         }
         int64_t entry;
