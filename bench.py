@@ -48,9 +48,9 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "70cb37f403b3f23687f45a1673605c387fed9211bcbeb4e08870765e8f548161",
-    "fetch_kib": 278653.406, "fetch_scale": 524288 / 262165.375,
-    "write_kib": 4177.703, "write_scale": 524288 / 524288.0,
+    "sha256": "64e3be859c398c3c5c54f25b549b035025dab4a9ae97a11fe5623351828a913b",
+    "fetch_kib": 278658.448, "fetch_scale": 524288 / 262165.5625,
+    "write_kib": 4096.771, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -61,9 +61,9 @@ ATTN64_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "8a63e0c5e189c6be919c9028678285997c3a720984a736a968e2e50247145ac3",
-    "fetch_kib": 44253.595, "fetch_scale": 524288 / 262161.875,
-    "write_kib": 32919.541, "write_scale": 524288 / 524288.0,
+    "sha256": "d3fd69d3c2a262794876e29633038667d4e3325b0b0fcabe4ea637f896a21cfa",
+    "fetch_kib": 44717.473, "fetch_scale": 524288 / 262161.9375,
+    "write_kib": 32920.742, "write_scale": 524288 / 524288.0,
 }
 
 
