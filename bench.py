@@ -48,7 +48,7 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "64e3be859c398c3c5c54f25b549b035025dab4a9ae97a11fe5623351828a913b",
+    "sha256": "cbdd990f658a3f37eab056de39f98ee059c0dc5d4dafe7744db6185865287ac3",
     "fetch_kib": 278658.448, "fetch_scale": 524288 / 262165.5625,
     "write_kib": 4096.771, "write_scale": 524288 / 524288.0,
 }

@@ -345,7 +345,9 @@ score_rows_kernel(ScoreArgs a, int32_t n_rows) {
             const float y = odd ? pa : pb;
             const float score = x + swap_rows16(y);
             if (MODE == kScoreFlat) {
-              if (e < wr_nv[p2]) out[p2][e] = score_key(score);
+              // every score is written once and read once by the selection:
+              // non-temporal, like the selection's loads of them
+              if (e < wr_nv[p2]) __builtin_nontemporal_store(score_key(score), &out[p2][e]);
             } else {
               // maximum over the visible entries of each block of 8 (lanes
               // c .. c + 7 of a 16-lane row hold one block of one row)
@@ -536,7 +538,7 @@ select_kernel(SelectArgs a) {
 #pragma unroll
   for (int j = 0; j < kKeys; ++j) {
     const int i = base + 64 * j;
-    key[j] = i < n_ld ? kin[i] : 0u;
+    key[j] = i < n_ld ? __builtin_nontemporal_load(&kin[i]) : 0u;   // read once
   }
   int32_t ids[IDS ? kKeys : 1];
   if (IDS) {
