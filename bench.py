@@ -84,6 +84,8 @@ def scan_traffic_bytes():
     sources changed since the counters were taken."""
     return counter_traffic_bytes(SCAN_COUNTERS)
 SCALE = 1.0 / math.sqrt(512)
+# input sets the timed steps cycle through (queries, indexer weights, SWA rows)
+N_INPUT_SETS = 4
 
 
 def parse():
@@ -146,11 +148,6 @@ def build(ctx_override=None, wid=3):
         csa2=csa2, wl=wl, B=B, T=T, H=H, L=L, cache=cache, new_lat=new_lat, new_ik=new_ik,
         new_dst=torch.arange(B, dtype=torch.int64, device=dev) * T + (T - 1),
         row_seq=i32(list(range(B))), row_nvis=i32([T] * B),
-        q=[W.bf16_normal((B, H, 512), W.seed_for(seed, W.T_Q, l), device=dev) for l in range(L)],
-        q_idx=[W.bf16_normal((B, 8, 128), W.seed_for(seed, W.T_QIDX, l), device=dev) for l in range(L)],
-        w=[W.uniform01((B, 8), W.seed_for(seed, W.T_W, l), device=dev) for l in range(L)],
-        swa=[csa2.Swa(W.swa_rows_e4m3(B * wl.swa, 512, W.seed_for(seed, W.T_SWA, l), device=dev)
-                      .reshape(B, wl.swa, 512), i32([wl.swa] * B), wl.swa) for l in range(L)],
         block_keys=csa2.block_keys_buffer(B, T),
         pool=torch.empty((B, wl.k_blk), dtype=torch.int32, device=dev),
         n_pool=torch.empty(B, dtype=torch.int32, device=dev),
@@ -162,8 +159,29 @@ def build(ctx_override=None, wid=3):
         o=torch.empty((B, H, 512), dtype=torch.float32, device=dev),
         lse=torch.empty((B, H), dtype=torch.float32, device=dev),
     )
+    # input sets: every layer's queries, indexer weights and SWA window, drawn
+    # afresh per set (set 0 from the layer's own seeds); the timed steps cycle
+    # through the sets, so consecutive steps gather different entries and read
+    # different SWA rows instead of finding the previous step's in the caches
+    def input_set(k):
+        sd = lambda t, l: W.seed_for(seed, t, l, k)
+        return dict(
+            q=[W.bf16_normal((B, H, 512), sd(W.T_Q, l), device=dev) for l in range(L)],
+            q_idx=[W.bf16_normal((B, 8, 128), sd(W.T_QIDX, l), device=dev) for l in range(L)],
+            w=[W.uniform01((B, 8), sd(W.T_W, l), device=dev) for l in range(L)],
+            swa=[csa2.Swa(W.swa_rows_e4m3(B * wl.swa, 512, sd(W.T_SWA, l), device=dev)
+                          .reshape(B, wl.swa, 512), i32([wl.swa] * B), wl.swa) for l in range(L)])
+
+    ctx["sets"] = [input_set(k) for k in range(N_INPUT_SETS)]
+    use_set(ctx, 0)
     torch.cuda.synchronize()
     return ctx
+
+
+def use_set(c, k):
+    """Makes input set k the one the step reads (q, q_idx, w, swa per layer)."""
+    for name in ("q", "q_idx", "w", "swa"):
+        c[name] = c["sets"][k][name]
 
 
 def _append(c):
@@ -245,12 +263,15 @@ def _outputs(c):
 
 
 def run_gpu(c, steps, warmup, eager):
-    """Times `steps` steps after `warmup` untimed ones.  Returns the wall time,
-    the scan kernel's mean event time (ms), and the per-layer event times (ms)
-    of a separate eager pass."""
+    """Times `steps` steps after `warmup` untimed ones, the steps cycling
+    through the input sets.  Returns the wall time, the scan kernel's mean
+    event time (ms), and the per-layer event times (ms) of a separate eager
+    pass."""
     import torch
 
-    for _ in range(warmup):
+    n_sets = len(c["sets"])
+    for i in range(warmup):
+        use_set(c, i % n_sets)
         step(c)
     torch.cuda.synchronize()
     L = c["L"]
@@ -258,7 +279,8 @@ def run_gpu(c, steps, warmup, eager):
     evs = [dict(scan0=torch.cuda.Event(enable_timing=True), scan1=torch.cuda.Event(enable_timing=True),
                 start=torch.cuda.Event(enable_timing=True),
                 layer=[torch.cuda.Event(enable_timing=True) for _ in range(L)]) for _ in range(3)]
-    for e in evs:
+    for j, e in enumerate(evs):
+        use_set(c, j % n_sets)
         e["start"].record()
         step(c, e)
     torch.cuda.synchronize()
@@ -268,33 +290,42 @@ def run_gpu(c, steps, warmup, eager):
         for l in range(L):
             per_layer[l] += prev.elapsed_time(e["layer"][l]) / len(evs)
             prev = e["layer"][l]
-    ref = _outputs(c)
     graphs = None
     if not eager:
-        graphs = capture(c)
-        for g in graphs:
+        use_set(c, 0)
+        step(c)
+        torch.cuda.synchronize()
+        ref = _outputs(c)
+        graphs = []
+        for k in range(n_sets):            # one set of graphs per input set
+            use_set(c, k)
+            graphs.append(capture(c))
+        for g in graphs[0]:
             g.replay()
         torch.cuda.synchronize()
         for a, b in zip(ref, _outputs(c)):
             if not torch.equal(a, b):
                 raise RuntimeError("graph replay differs from the eager step")
-        for _ in range(warmup):
-            for g in graphs:
+        for i in range(warmup):
+            for g in graphs[i % n_sets]:
                 g.replay()
     scan = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
         if graphs is None:
+            use_set(c, k % n_sets)
             step(c, dict(scan0=scan[k][0], scan1=scan[k][1], layer=[_NoEvent] * L))
         else:
-            graphs[0].replay()
+            g = graphs[k % n_sets]
+            g[0].replay()
             scan[k][0].record()
-            graphs[1].replay()
+            g[1].replay()
             scan[k][1].record()
-            graphs[2].replay()
+            g[2].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    use_set(c, 0)
     scan_ms = sum(a.elapsed_time(b) for a, b in scan) / steps
     return wall, scan_ms, per_layer
 
