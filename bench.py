@@ -12,7 +12,8 @@ with its own 16-head query and its own 128-row FP8 SWA window
             attention + SWA;
   Reuse   : attention + SWA over the last Reindex layer's Top-512.
 Inputs are seeded synthetic tensors already resident in HBM; the cache
-(8 x 1M entries x 356 B) is built before timing.
+(8 x 1M entries x 356 B) is built before timing, and the timed steps cycle
+through four input sets (each layer's queries, indexer weights and SWA rows).
 
 The timed steps launch every kernel from Python (the GPU, not the host, is
 the limit: replaying the step as HIP graphs measured no faster); --graph
