@@ -616,30 +616,30 @@ def path_flops_per_query(T, wl):
 
 def pages_figures(c, step_ms_1m=None, step_ms_4k=None):
     """The pages' own figures (no hardware stated for any) beside what this
-    build's layout and launch plan give, and the measured step-time ratio of
-    the same 20-layer decode stack at 1M and at 4K context when given."""
+    library's layout and launch plan give, and the measured step-time ratio
+    of the same 20-layer decode stack at 1M and at 4K context when given."""
     csa2, wl = c["csa2"], c["wl"]
     per_entry = c["cache"].nbytes // (c["B"] * c["T"])
     split = csa2.csa2_attn_workspace_size(c["B"], c["H"], wl.k_pos, wl.swa) > 0
     return {
-        "bytes_per_entry": {"this_build": per_entry, "pages": 356},
-        "bytes_per_token_at_2_5_entries": {"this_build": per_entry * 2.5, "pages": 890},
+        "bytes_per_entry": {"csa2_amd": per_entry, "pages": 356},
+        "bytes_per_token_at_2_5_entries": {"csa2_amd": per_entry * 2.5, "pages": 890},
         "kernels_per_reuse_layer_decode": {
-            "this_build": 2 if split else 1,
+            "csa2_amd": 2 if split else 1,
             "pages": 11,
             "note": "ours: sparse attention with the SWA branch fused (+ the split merge at this batch); "
                     "the pages count the whole fused layer"},
         "kernels_per_reuse_layer_prefill": {
-            "this_build": 1 if csa2.csa2_attn_workspace_size(4096, c["H"], wl.k_pos, wl.swa) == 0 else 2,
+            "csa2_amd": 1 if csa2.csa2_attn_workspace_size(4096, c["H"], wl.k_pos, wl.swa) == 0 else 2,
             "pages": 15,
             "note": "ours at the 4,096-query prefill chunk: one attention launch with the SWA branch fused"},
         "decode_flops_1m_over_4k": {
-            "this_build": round(path_flops_per_query(1 << 20, wl) / path_flops_per_query(4096, wl), 3),
+            "csa2_amd": round(path_flops_per_query(1 << 20, wl) / path_flops_per_query(4096, wl), 3),
             "pages": 1.25,
             "note": "ours: the CSA2 path alone (indexer scan, re-scores, attention of the 20-layer stack); "
                     "the pages: the whole model"},
         "decode_step_time_1m_over_4k": {
-            "this_build": round(step_ms_1m / step_ms_4k, 3) if step_ms_1m and step_ms_4k else None,
+            "csa2_amd": round(step_ms_1m / step_ms_4k, 3) if step_ms_1m and step_ms_4k else None,
             "ms_at_4k": round(step_ms_4k, 4) if step_ms_4k else None,
             "note": "measured: the same 20-layer decode step (batch 8) at 4,096 and at 1,048,576 entries"},
     }

@@ -36,7 +36,7 @@ def test_pages_figures_from_the_cache_layout():
 
     c = dict(csa2=csa2, wl=W.WORKLOADS[3], cache=Planes(), B=8, T=1000, H=16)
     f = bench.pages_figures(c)
-    assert f["bytes_per_entry"] == {"this_build": 356, "pages": 356}
-    assert f["bytes_per_token_at_2_5_entries"]["this_build"] == 890
-    assert f["kernels_per_reuse_layer_decode"]["this_build"] == 2     # attention + split merge at batch 8
-    assert abs(f["decode_flops_1m_over_4k"]["this_build"] - 2_734_686_208 / 469_762_048) < 1e-3
+    assert f["bytes_per_entry"] == {"csa2_amd": 356, "pages": 356}
+    assert f["bytes_per_token_at_2_5_entries"]["csa2_amd"] == 890
+    assert f["kernels_per_reuse_layer_decode"]["csa2_amd"] == 2     # attention + split merge at batch 8
+    assert abs(f["decode_flops_1m_over_4k"]["csa2_amd"] - 2_734_686_208 / 469_762_048) < 1e-3
