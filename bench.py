@@ -62,9 +62,9 @@ ATTN64_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "d3fd69d3c2a262794876e29633038667d4e3325b0b0fcabe4ea637f896a21cfa",
-    "fetch_kib": 44803.250, "fetch_scale": 524288 / 262162.375,
-    "write_kib": 32939.617, "write_scale": 524288 / 524288.0,
+    "sha256": "7a13f0e41b30ea480a7ea9a7e22009909d9bf0cde91812a874089ffadf4908c6",
+    "fetch_kib": 45133.791, "fetch_scale": 524288 / 262166.4375,
+    "write_kib": 32963.557, "write_scale": 524288 / 524288.0,
 }
 
 

@@ -102,10 +102,41 @@ attn_kernel(AttnArgs a) {
   const int G = lane >> 4;
   const int c = lane & 15;
 
-  // the per-row scalars are read together (none waits on another)
+  constexpr int TK = kAttnTileKeys;
+  // this work-group's first tile
+  const int t_begin = split ? sp * a.tiles_per_split : 0;
+  const int32_t *topk = a.topk ? a.topk + (int64_t)r * a.k_pos : nullptr;
+  // The entry id of this lane's key in tile T, read ahead of need and without
+  // waiting for n_topk (every slot below k_pos is inside the row).
+  auto load_id = [&](int T) -> int32_t {
+    const int slot = T * TK + 16 * w + c;
+    return (topk && slot < a.k_pos) ? topk[slot] : -1;
+  };
+  // The ids of the first three tiles and Q go out before the per-row scalars:
+  // scalar loads return out of order, so a use of any of them waits for all,
+  // and these loads need none of them.
+  int32_t id0 = load_id(t_begin), id1 = load_id(t_begin + 1), id2 = load_id(t_begin + 2);
+  uint4 q_raw[16];
+  {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * HT + h0 + c) * 512 + 128 * G);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) q_raw[t] = qp[t];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the per-row scalars are read together and unconditionally (an absent
+  // array is stood in for by row_seq); the empty asm takes all three at this
+  // point, so one wait covers them and no load is moved into a branch that
+  // depends on another
+  const int32_t *ntp = a.topk ? a.n_topk : a.row_seq;
+  const int32_t *sep = a.swa_kv ? a.swa_end : a.row_seq;
   int seq = a.row_seq[r];
-  int n_g = a.topk ? a.n_topk[r] : 0;
-  int64_t end = a.swa_kv ? a.swa_end[r] : 0;
+  int n_g = ntp[r];
+  int end32 = sep[r];
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::"s"(seq), "s"(n_g), "s"(end32));
+  n_g = a.topk ? n_g : 0;
+  int64_t end = a.swa_kv ? end32 : 0;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   if (!seq_ok) seq = 0;
   n_g = (!seq_ok || n_g < 0) ? 0 : (n_g > a.k_pos ? a.k_pos : n_g);
@@ -117,22 +148,17 @@ attn_kernel(AttnArgs a) {
     s0 = s0 < 0 ? 0 : s0;
     n_s = (int)(end - s0);
   }
-  constexpr int TK = kAttnTileKeys;
   const int n_gt = (n_g + TK - 1) / TK;
   const int n_all = n_gt + (n_s + TK - 1) / TK;
   // this work-group's tiles: [t_begin, t_end)
-  const int t_begin = split ? sp * a.tiles_per_split : 0;
   int t_end = split ? t_begin + a.tiles_per_split : n_all;
   t_end = t_end < n_all ? t_end : n_all;
 
   // Q operand: qa[t] = q[r][h0 + c][128G + 8t .. +7] in f16, t < 16 (the
   // contraction over the 512 channels runs in this lane-consistent order)
   f16x8 qa[16];
-  {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)r * HT + h0 + c) * 512 + 128 * G);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) qa[t] = bf16x8_to_f16(qp[t]);
-  }
+  for (int t = 0; t < 16; ++t) qa[t] = bf16x8_to_f16(q_raw[t]);
 
   // Accumulators, lane (G, c), block db: OT: O[head h0 + c][channels
   // 128w + 16db + 4G .. +3] (four consecutive channels of one head, stored
@@ -176,14 +202,7 @@ attn_kernel(AttnArgs a) {
   const uint8_t *kv_codes = a.kv_codes + (int64_t)seq * a.cap * 256;
   const uint8_t *kv_scales = a.kv_scales + (int64_t)seq * a.cap * 32;
   const uint8_t *swa = a.swa_kv ? a.swa_kv + ((int64_t)seq * a.swa_len) * 512 : nullptr;
-  const int32_t *topk = a.topk ? a.topk + (int64_t)r * a.k_pos : nullptr;
 
-  // The entry id of this lane's key in tile T, read ahead of need and without
-  // waiting for n_topk (every slot below k_pos is inside the row).
-  auto load_id = [&](int T) -> int32_t {
-    const int slot = T * TK + 16 * w + c;
-    return (topk && slot < a.k_pos) ? topk[slot] : -1;
-  };
   auto load_fp4 = [&](int T, int32_t id) {
     KeyFp4 k;
     const int slot = T * TK + 16 * w + c;
@@ -330,10 +349,9 @@ attn_kernel(AttnArgs a) {
   // gathers are random HBM reads); the tile registers rotate by copy.
   const int g_end = t_end < n_gt ? t_end : n_gt;
   {
-    int32_t id2 = load_id(t_begin + 2);
     KeyFp4 ka, kb;
-    if (t_begin < g_end) ka = load_fp4(t_begin, load_id(t_begin));
-    if (t_begin + 1 < g_end) kb = load_fp4(t_begin + 1, load_id(t_begin + 1));
+    if (t_begin < g_end) ka = load_fp4(t_begin, id0);
+    if (t_begin + 1 < g_end) kb = load_fp4(t_begin + 1, id1);
     for (int T = t_begin; T < g_end; ++T) {
       dequant_fp4(ka);
       const bool v = ka.valid;

@@ -123,10 +123,19 @@ attn_h64_kernel(AttnArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // the per-row scalars are read together (none waits on another)
+  // the per-row scalars are read together and unconditionally (an absent
+  // array is stood in for by row_seq); the empty asm takes all three at this
+  // point, so one wait covers them and no load is moved into a branch that
+  // depends on another
+  const int32_t *ntp = a.topk ? a.n_topk : a.row_seq;
+  const int32_t *sep = a.swa_kv ? a.swa_end : a.row_seq;
   int seq = a.row_seq[r];
-  int n_g = a.topk ? a.n_topk[r] : 0;
-  int64_t end = a.swa_kv ? a.swa_end[r] : 0;
+  int n_g = ntp[r];
+  int end32 = sep[r];
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::"s"(seq), "s"(n_g), "s"(end32));
+  n_g = a.topk ? n_g : 0;
+  int64_t end = a.swa_kv ? end32 : 0;
   const bool seq_ok = seq >= 0 && seq < a.n_seq;
   if (!seq_ok) seq = 0;
   n_g = (!seq_ok || n_g < 0) ? 0 : (n_g > a.k_pos ? a.k_pos : n_g);
