@@ -49,7 +49,7 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "cbdd990f658a3f37eab056de39f98ee059c0dc5d4dafe7744db6185865287ac3",
+    "sha256": "7c39adcb03dd80f7366099ff6f11d84eb8663420dd902e5bea7be11cb367c653",
     "fetch_kib": 278658.448, "fetch_scale": 524288 / 262165.5625,
     "write_kib": 4096.771, "write_scale": 524288 / 524288.0,
 }

@@ -150,11 +150,13 @@ score_kernel(ScoreArgs a) {
         }
         int64_t entry;
         if (MODE == kScorePool) {
-          // the pool id is read whether or not p < n_pool (every p below
-          // k_blocks is inside the pool row), so the read need not wait for
-          // the count
+          // the pool id is read whether or not p < n_pool, so the read need
+          // not wait for the count; p is clamped into the row (the tiles
+          // after the first of a group can start past the row's 8 k_blocks
+          // slots, and such slots are masked: p >= k_blocks >= n_pool)
           const int64_t p = slot[u] >> 3;
-          const int b = a.pool_blocks[(int64_t)r * a.k_blocks + p];
+          const int64_t pc = p < a.k_blocks ? p : (int64_t)a.k_blocks - 1;
+          const int b = a.pool_blocks[(int64_t)r * a.k_blocks + pc];
           entry = (int64_t)b * 8 + (slot[u] & 7);
           valid[u] = (p < np) && b >= 0 && entry < n_vis;
         } else {
