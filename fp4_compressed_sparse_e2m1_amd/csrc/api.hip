@@ -2,8 +2,6 @@
 // The operations and their sources are documented in include/csa2.h.
 #include <math.h>
 
-#include <mutex>
-
 #include "../../include/csa2.h"
 #include "internal.h"
 
@@ -84,17 +82,6 @@ Layout plan_workspace(int32_t op, int32_t rows, int32_t max_nvis, int32_t k_bloc
   off += half;
   L.total = off;
   return L;
-}
-
-std::once_flag g_prepare_once;
-hipError_t g_prepare_status = hipSuccess;
-
-hipError_t prepare() {
-  std::call_once(g_prepare_once, [] {
-    g_prepare_status = prepare_select();
-    if (g_prepare_status == hipSuccess) g_prepare_status = prepare_attention();
-  });
-  return g_prepare_status;
 }
 
 struct SelectOut {
@@ -215,7 +202,6 @@ csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_i
   if (op == CSA2_OP_INDEX_REINDEX && pool_mode && (!pool_in || !n_pool_in)) return CSA2_E_INVALID_ARG;
   const Layout L = plan_workspace(op, n_rows, max_nvis, k_blocks, k_pos);
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
-  if (prepare() != hipSuccess) return CSA2_E_HIP;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -377,7 +363,6 @@ csa2_status csa2_index_scan(const csa2_cache *cache, const uint16_t *q_idx, cons
   const csa2_status cs = check_index_args(cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis);
   if (cs != CSA2_OK) return cs;
   if (!block_keys || !aligned(block_keys, 4)) return CSA2_E_INVALID_ARG;
-  if (prepare() != hipSuccess) return CSA2_E_HIP;
   ScoreArgs sa = score_args(cache, q_idx, w, row_seq, row_nvis, max_nvis);
   const int64_t nb = ((int64_t)max_nvis + 7) / 8;
   sa.keys_out = block_keys;
@@ -447,7 +432,6 @@ csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t
   const csa2_status ws = attach_workspace(a, n_rows, n_heads, k_pos, swa ? swa->window : 0,
                                           workspace, workspace_bytes);
   if (ws != CSA2_OK) return ws;
-  if (prepare() != hipSuccess) return CSA2_E_HIP;
   hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
 }
@@ -477,7 +461,6 @@ csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *ro
   const csa2_status ws = attach_workspace(a, n_rows, n_heads, 0, swa->window, workspace,
                                           workspace_bytes);
   if (ws != CSA2_OK) return ws;
-  if (prepare() != hipSuccess) return CSA2_E_HIP;
   hipError_t e = launch_attention(a, n_heads, n_rows, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
 }

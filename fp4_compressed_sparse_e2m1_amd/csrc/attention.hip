@@ -540,7 +540,6 @@ attn_merge_kernel(AttnArgs a, int H) {
 
 }  // namespace
 
-hipError_t prepare_attention() { return hipSuccess; }
 
 AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t window) {
   // keys per tile of the kernel that serves this head count

@@ -945,7 +945,6 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int6
   return hipGetLastError();
 }
 
-hipError_t prepare_select() { return hipSuccess; }
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
                          bool wide, hipStream_t stream) {

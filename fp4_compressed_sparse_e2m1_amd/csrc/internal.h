@@ -7,6 +7,14 @@
 
 namespace csa2 {
 
+// Work-groups of a grid-stride launch over `items` work-items: enough to fill
+// the chip many times over, bounded so the grid never exceeds what one launch
+// dimension takes.
+inline unsigned grid_blocks(int64_t items, int threads) {
+  const int64_t b = (items + threads - 1) / threads;
+  return (unsigned)(b < (1 << 18) ? (b > 0 ? b : 1) : (1 << 18));
+}
+
 // ---------------------------------------------------------------- indexer
 enum ScoreMode { kScoreBlockMax = 0, kScoreFlat = 1, kScorePool = 2 };
 
@@ -71,7 +79,6 @@ constexpr int kMaxPoolBlocks = 4096;
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
                          bool wide, hipStream_t stream);
-hipError_t prepare_select();
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
@@ -122,7 +129,6 @@ hipError_t launch_attention(const AttnArgs &a, int32_t n_heads, int32_t n_rows, 
 // caller sets n_heads = 64, n_hgroups = 1 and n_rows).  Built in its own
 // translation unit: its O accumulators stay in the matrix-core registers.
 hipError_t launch_attention_h64(const AttnArgs &a, int64_t blocks, hipStream_t stream);
-hipError_t prepare_attention();
 
 // ---------------------------------------------------------------- quantise
 hipError_t launch_quantize(const float *x, int64_t n, int dim, int group, const int64_t *dst_rows,

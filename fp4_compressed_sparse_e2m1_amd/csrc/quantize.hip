@@ -14,7 +14,8 @@
 //    3.5, 5}.  The scale has at most 4 significant bits and each constant at
 //    most 3, so every threshold product is exact in fp32.
 // One thread encodes one group; consecutive threads take consecutive groups
-// of a row, so the fp32 reads and the code writes are coalesced.
+// of a row, so the fp32 reads and the code writes are coalesced.  The grid is
+// bounded (grid_blocks) and strides over larger inputs.
 #include "device.h"
 #include "internal.h"
 
@@ -91,14 +92,16 @@ __global__ void __launch_bounds__(256)
 quantize_kernel(const float *__restrict__ x, int64_t n, int dim, const int64_t *__restrict__ dst_rows,
                 uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, int64_t plane_rows) {
   const int ngroups = dim / G;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n * ngroups) return;
-  const int64_t r = idx / ngroups;
-  const int g = (int)(idx - r * ngroups);
-  const int64_t dst = dst_rows ? dst_rows[r] : r;
-  if (dst < 0 || dst >= plane_rows) return;
-  encode_group<G>(x + r * dim + (int64_t)g * G, codes + dst * (dim / 2) + (int64_t)g * (G / 2),
-                  scales + dst * ngroups + g);
+  const int64_t total = n * ngroups;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / ngroups;
+    const int g = (int)(idx - r * ngroups);
+    const int64_t dst = dst_rows ? dst_rows[r] : r;
+    if (dst < 0 || dst >= plane_rows) continue;
+    encode_group<G>(x + r * dim + (int64_t)g * G, codes + dst * (dim / 2) + (int64_t)g * (G / 2),
+                    scales + dst * ngroups + g);
+  }
 }
 
 // Appends n entries to both planes of a cache in one launch: threads
@@ -109,20 +112,22 @@ append_kernel(const float *__restrict__ lat, const float *__restrict__ ik, int64
               const int64_t *__restrict__ dst_rows, uint8_t *__restrict__ kv_codes,
               uint8_t *__restrict__ kv_scales, uint8_t *__restrict__ ik_codes,
               uint8_t *__restrict__ ik_scales, int64_t plane_rows) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < n * 32) {
-    const int64_t r = idx >> 5;
-    const int g = (int)(idx & 31);
-    const int64_t dst = dst_rows[r];
-    if (dst < 0 || dst >= plane_rows) return;
-    encode_group<16>(lat + r * 512 + g * 16, kv_codes + dst * 256 + g * 8, kv_scales + dst * 32 + g);
-  } else if (idx < n * 36) {
-    const int64_t j = idx - n * 32;
-    const int64_t r = j >> 2;
-    const int g = (int)(j & 3);
-    const int64_t dst = dst_rows[r];
-    if (dst < 0 || dst >= plane_rows) return;
-    encode_group<32>(ik + r * 128 + g * 32, ik_codes + dst * 64 + g * 16, ik_scales + dst * 4 + g);
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n * 36;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    if (idx < n * 32) {
+      const int64_t r = idx >> 5;
+      const int g = (int)(idx & 31);
+      const int64_t dst = dst_rows[r];
+      if (dst < 0 || dst >= plane_rows) continue;
+      encode_group<16>(lat + r * 512 + g * 16, kv_codes + dst * 256 + g * 8, kv_scales + dst * 32 + g);
+    } else {
+      const int64_t j = idx - n * 32;
+      const int64_t r = j >> 2;
+      const int g = (int)(j & 3);
+      const int64_t dst = dst_rows[r];
+      if (dst < 0 || dst >= plane_rows) continue;
+      encode_group<32>(ik + r * 128 + g * 32, ik_codes + dst * 64 + g * 16, ik_scales + dst * 4 + g);
+    }
   }
 }
 
@@ -131,8 +136,7 @@ append_kernel(const float *__restrict__ lat, const float *__restrict__ ik, int64
 hipError_t launch_quantize(const float *x, int64_t n, int dim, int group, const int64_t *dst_rows,
                            uint8_t *codes, uint8_t *scales, int64_t plane_rows, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int64_t total = n * (dim / group);
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const unsigned blocks = grid_blocks(n * (dim / group), 256);
   if (group == 16)
     quantize_kernel<16><<<blocks, 256, 0, stream>>>(x, n, dim, dst_rows, codes, scales, plane_rows);
   else
@@ -144,7 +148,7 @@ hipError_t launch_append(const float *lat, const float *ik, int64_t n, const int
                          uint8_t *kv_codes, uint8_t *kv_scales, uint8_t *ik_codes, uint8_t *ik_scales,
                          int64_t plane_rows, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n * 36 + 255) / 256);
+  const unsigned blocks = grid_blocks(n * 36, 256);
   append_kernel<<<blocks, 256, 0, stream>>>(lat, ik, n, dst_rows, kv_codes, kv_scales, ik_codes, ik_scales,
                                             plane_rows);
   return hipGetLastError();

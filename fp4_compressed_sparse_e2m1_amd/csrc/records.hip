@@ -6,7 +6,8 @@
 //
 // One thread per 4-byte word: a record is 89 words (64 + 8 + 16 + 1), every
 // plane row is a whole number of words, and consecutive threads write (or
-// read) consecutive record words.
+// read) consecutive record words; the grid is bounded and strides over
+// longer ranges.
 #include "device.h"
 #include "internal.h"
 
@@ -20,24 +21,25 @@ template <bool TO_RECORDS>
 __global__ void __launch_bounds__(kRecordThreads)
 records_kernel(uint32_t *kv_codes, uint32_t *kv_scales, uint32_t *ik_codes, uint32_t *ik_scales,
                int64_t plane_row0, int64_t count, uint32_t *records) {
-  const int64_t t = (int64_t)blockIdx.x * kRecordThreads + threadIdx.x;
-  if (t >= count * kRecordWords) return;
-  const int64_t e = t / kRecordWords;
-  const int w = (int)(t - e * kRecordWords);
-  const int64_t row = plane_row0 + e;
-  uint32_t *p;
-  if (w < 64)
-    p = kv_codes + row * 64 + w;
-  else if (w < 72)
-    p = kv_scales + row * 8 + (w - 64);
-  else if (w < 88)
-    p = ik_codes + row * 16 + (w - 72);
-  else
-    p = ik_scales + row;
-  if (TO_RECORDS)
-    records[t] = *p;
-  else
-    *p = records[t];
+  for (int64_t t = (int64_t)blockIdx.x * kRecordThreads + threadIdx.x; t < count * kRecordWords;
+       t += (int64_t)gridDim.x * kRecordThreads) {
+    const int64_t e = t / kRecordWords;
+    const int w = (int)(t - e * kRecordWords);
+    const int64_t row = plane_row0 + e;
+    uint32_t *p;
+    if (w < 64)
+      p = kv_codes + row * 64 + w;
+    else if (w < 72)
+      p = kv_scales + row * 8 + (w - 64);
+    else if (w < 88)
+      p = ik_codes + row * 16 + (w - 72);
+    else
+      p = ik_scales + row;
+    if (TO_RECORDS)
+      records[t] = *p;
+    else
+      *p = records[t];
+  }
 }
 
 }  // namespace
@@ -46,8 +48,7 @@ hipError_t launch_records(bool to_records, uint8_t *kv_codes, uint8_t *kv_scales
                           uint8_t *ik_scales, int64_t plane_row0, int64_t count, uint8_t *records,
                           hipStream_t stream) {
   if (count == 0) return hipSuccess;
-  const int64_t words = count * kRecordWords;
-  const dim3 grid((unsigned)((words + kRecordThreads - 1) / kRecordThreads));
+  const dim3 grid(grid_blocks(count * kRecordWords, kRecordThreads));
   auto w32 = [](uint8_t *x) { return reinterpret_cast<uint32_t *>(x); };
   if (to_records)
     records_kernel<true><<<grid, kRecordThreads, 0, stream>>>(w32(kv_codes), w32(kv_scales), w32(ik_codes),

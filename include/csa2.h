@@ -34,8 +34,11 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued on it; CSA2_OK means "validated and enqueued".  Device faults
  *     show up at the caller's next synchronisation.
- *   - Arguments are validated on the host before anything is launched; on an
- *     error status nothing has been written or launched.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation status (CSA2_E_INVALID_ARG, CSA2_E_UNSUPPORTED,
+ *     CSA2_E_WORKSPACE) nothing has been written or launched.  CSA2_E_HIP
+ *     reports a failed launch; a call that enqueues several kernels may have
+ *     enqueued the ones before the failing one.
  *   - Device-side counts (row_nvis, n_pool, n_topk, SWA ends) are clamped to
  *     the host-side maxima; out-of-range sequence ids make a row empty;
  *     entry ids outside [0, cap) are skipped.  These guards keep every access

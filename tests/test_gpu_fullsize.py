@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import check_attention, check_selection
+from tests.parity import check_attention, check_full_row, check_reindex_row, check_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -105,30 +105,17 @@ def test_decode_b8_1m_full_reindex_reuse(csa2):
         # the whole 1M-entry indexer plane of this sequence, bit for bit
         np.testing.assert_array_equal(c["cache"].ik_codes[s].cpu().numpy(), ikc)
         np.testing.assert_array_equal(c["cache"].ik_scales[s].cpu().numpy(), iks)
-        bs = f["block_scores"]
-        check_selection(pool[s], npool[s], f["pool"], len(f["pool"]), lambda b: bs[b], "pool")
-        sc = dict(zip(f["cand"].tolist(), f["cand_scores"].tolist()))
-        check_selection(topk[0][s], ntopk[0][s], f["topk"], f["n_topk"], lambda j: sc[j], "full topk")
+        check_full_row(csa2, c["cache"], c["q_idx"][0][s:s + 1], c["w"][0][s:s + 1], s, T, pool[s],
+                       npool[s], topk[0][s], ntopk[0][s], f, wl.k_blk, wl.k_pos, f"full row {s}")
         oracle_topk[(s, 0)] = f["topk"]
-        same_pool = np.array_equal(pool[s][:npool[s]], f["pool"])
         for l, mode in enumerate(wl.layers):
             if mode != "reindex":
                 continue
             ref = oracle.reindex_select(qi[l][s], wv[l][s], ikc, iks, T, f["pool"], wl.k_pos)
             oracle_topk[(s, l)] = ref["topk"]
-            sc = dict(zip(ref["cand"].tolist(), ref["cand_scores"].tolist()))
-            if same_pool:
-                got, n = topk[l][s], ntopk[l][s]
-            else:                       # an accepted pool tie swap: re-run on the oracle's pool
-                pb = np.full((B, wl.k_blk), -1, np.int32)
-                pb[:, :len(f["pool"])] = f["pool"]
-                tk = torch.empty((B, wl.k_pos), dtype=torch.int32, device="cuda")
-                nt = torch.empty(B, dtype=torch.int32, device="cuda")
-                csa2.csa2_index_reindex(c["cache"], c["q_idx"][l], c["w"][l], c["row_seq"],
-                                        c["row_nvis"], T, i32(pb), i32([len(f["pool"])] * B),
-                                        wl.k_blk, wl.k_pos, tk, nt, c["ws_re"])
-                got, n = tk.cpu().numpy()[s], nt.cpu().numpy()[s]
-            check_selection(got, n, ref["topk"], ref["n_topk"], lambda j: sc[j], f"reindex {l}")
+            check_reindex_row(csa2, c["cache"], c["q_idx"][l][s:s + 1], c["w"][l][s:s + 1], s, T,
+                              pool[s], npool[s], topk[l][s], ntopk[l][s], ref, f["pool"], wl.k_blk,
+                              wl.k_pos, f"reindex layer {l} row {s}")
     # attention of a Full, a Reindex and a Reuse layer over the oracle's lists
     for l in (0, 2, 10):
         src = l if wl.layers[l] != "reuse" else 4
@@ -186,11 +173,8 @@ def test_multi_query_scan_1m(csa2):
         lambda sr: oracle.full_layer_select(qi[sr[1]], wv[sr[1]], *planes[sr[0]], int(nvis_h[sr[1]]),
                                             wl.k_blk, wl.k_pos), jobs, len(jobs))
     for (s, r), f in zip(jobs, refs):
-        bs = f["block_scores"]
-        check_selection(pool_h[r], npool_h[r], f["pool"], len(f["pool"]), lambda b: bs[b], f"pool row {r}")
-        if np.array_equal(pool_h[r][:npool_h[r]], f["pool"]):
-            sc = dict(zip(f["cand"].tolist(), f["cand_scores"].tolist()))
-            check_selection(topk_h[r], ntopk_h[r], f["topk"], f["n_topk"], lambda j: sc[j], f"topk row {r}")
+        check_full_row(csa2, c["cache"], q_idx[r:r + 1], w[r:r + 1], s, int(nvis_h[r]), pool_h[r],
+                       npool_h[r], topk_h[r], ntopk_h[r], f, wl.k_blk, wl.k_pos, f"row {r}")
 
 
 # ------------------------------------------------------ 128K decode, 18 Reindex
@@ -223,21 +207,21 @@ def test_decode_b32_128k_full_18_reindex(csa2):
     qi = [W.bf16_bits(x) for x in q_idx]
     wv = [x.cpu().numpy() for x in w]
     pool_h, npool_h = pool.cpu().numpy(), npool.cpu().numpy()
+    topk_h = [t.cpu().numpy() for t in topk]
+    ntopk_h = [t.cpu().numpy() for t in ntopk]
     for s in sample:
         ik = W.rms_rows(T, 128, W.seed_for(seed, W.T_IKEY, 0, s), device="cuda").cpu().numpy()
         ikc, iks = oracle.quantize(ik, 32)
         np.testing.assert_array_equal(cache.ik_codes[s].cpu().numpy(), ikc)
         f = oracle.full_layer_select(qi[0][s], wv[0][s], ikc, iks, T, wl.k_blk, wl.k_pos)
-        bs = f["block_scores"]
-        check_selection(pool_h[s], npool_h[s], f["pool"], len(f["pool"]), lambda b: bs[b], "pool")
         assert len(oracle.pool_entries(f["pool"], T)) == 16384      # the constant candidate bound
-        if not np.array_equal(pool_h[s][:npool_h[s]], f["pool"]):
-            continue                    # accepted tie swap; the stage tests cover re-indexing
-        for l in range(L):
-            ref = f if l == 0 else oracle.reindex_select(qi[l][s], wv[l][s], ikc, iks, T, f["pool"], wl.k_pos)
-            sc = dict(zip(ref["cand"].tolist(), ref["cand_scores"].tolist()))
-            check_selection(topk[l].cpu().numpy()[s], ntopk[l].cpu().numpy()[s], ref["topk"],
-                            ref["n_topk"], lambda j: sc[j], f"layer {l}")
+        check_full_row(csa2, cache, q_idx[0][s:s + 1], w[0][s:s + 1], s, T, pool_h[s], npool_h[s],
+                       topk_h[0][s], ntopk_h[0][s], f, wl.k_blk, wl.k_pos, f"full row {s}")
+        for l in range(1, L):
+            ref = oracle.reindex_select(qi[l][s], wv[l][s], ikc, iks, T, f["pool"], wl.k_pos)
+            check_reindex_row(csa2, cache, q_idx[l][s:s + 1], w[l][s:s + 1], s, T, pool_h[s],
+                              npool_h[s], topk_h[l][s], ntopk_h[l][s], ref, f["pool"], wl.k_blk,
+                              wl.k_pos, f"reindex layer {l} row {s}")
 
 
 # ----------------------------------------------------- encoder prefill chunk
@@ -269,8 +253,7 @@ def test_encoder_prefill_4k_rows_64k_ctx(csa2):
     refs = {}
     for r in sample:
         f = oracle.full_layer_select(qi[r], wv[r], ikc, iks, int(n_vis[r]), 0, wl.k_pos)
-        sc = f["entry_scores"]
-        check_selection(tk[r], nt[r], f["topk"], f["n_topk"], lambda j: sc[j], f"row {r}")
+        check_topk(tk[r], nt[r], f, f"row {r}")
         refs[r] = f["topk"]
     # attention + SWA over the last 128 tokens of each query (rows of the chunk's SWA buffer)
     swa_first = int(t[0]) - (wl.swa - 1)
