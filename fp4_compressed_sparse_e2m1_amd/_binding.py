@@ -66,6 +66,8 @@ def load():
         lib.csa2_workspace_size.restype = sz
         lib.csa2_index_full.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         lib.csa2_index_full.restype = ctypes.c_int
+        lib.csa2_index_full_noalloc.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P, P, P, P]
+        lib.csa2_index_full_noalloc.restype = ctypes.c_int
         lib.csa2_index_scan.argtypes = [P, P, P, P, P, i32, i32, P, P]
         lib.csa2_index_scan.restype = ctypes.c_int
         lib.csa2_index_pool.argtypes = [P, P, P, P, P, i32, i32, P, i32, i32, P, P, P, P, P, sz, P]
@@ -238,6 +240,26 @@ def csa2_index_full(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, k_block
         _ptr(topk, torch.int32, "topk", (R, k_pos)), _ptr(n_topk, torch.int32, "n_topk", (R,)),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check("csa2_index_full", st)
+
+
+def csa2_index_full_noalloc(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, k_blocks, k_pos,
+                            pool_blocks, n_pool, topk, n_topk, stream=None):
+    """csa2_index_full with the library's static per-device scratch instead of
+    a workspace (for callers that cannot allocate)."""
+    R = row_seq.shape[0]
+    cs = cache.struct()
+    st = load().csa2_index_full_noalloc(
+        ctypes.byref(cs), _ptr(q_idx, torch.bfloat16, "q_idx", (R, 8, 128)),
+        _ptr(w, torch.float32, "w", (R, 8)), _ptr(row_seq, torch.int32, "row_seq", (R,)),
+        _ptr(row_nvis, torch.int32, "row_nvis", (R,)), R, int(max_nvis), int(k_blocks), int(k_pos),
+        _ptr(pool_blocks, torch.int32, "pool_blocks", (R, k_blocks), allow_none=k_blocks == 0),
+        _ptr(n_pool, torch.int32, "n_pool", (R,), allow_none=k_blocks == 0),
+        _ptr(topk, torch.int32, "topk", (R, k_pos)), _ptr(n_topk, torch.int32, "n_topk", (R,)),
+        _stream(stream))
+    _check("csa2_index_full_noalloc", st)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def block_keys_buffer(n_rows: int, max_nvis: int, device="cuda"):

@@ -2,6 +2,8 @@
 // The operations and their sources are documented in include/csa2.h.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/csa2.h"
 #include "internal.h"
 
@@ -183,12 +185,13 @@ ScoreArgs score_args(const csa2_cache *cache, const uint16_t *q_idx, const float
   return sa;
 }
 
-csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_idx, const float *w,
-                        const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
-                        int32_t max_nvis, const uint32_t *ext_block_keys, const int32_t *pool_in,
-                        const int32_t *n_pool_in, int32_t k_blocks, int32_t k_pos,
-                        int32_t *pool_out, int32_t *n_pool_out, int32_t *topk, int32_t *n_topk,
-                        void *workspace, size_t workspace_bytes, void *stream_ptr) {
+// Every argument check of an indexer call except the workspace's.
+csa2_status check_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                          const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                          int32_t max_nvis, const uint32_t *ext_block_keys, const int32_t *pool_in,
+                          const int32_t *n_pool_in, int32_t k_blocks, int32_t k_pos,
+                          const int32_t *pool_out, const int32_t *n_pool_out, const int32_t *topk,
+                          const int32_t *n_topk) {
   const csa2_status cs = check_index_args(cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis);
   if (cs != CSA2_OK) return cs;
   if (!topk || !n_topk || k_pos < 1 || k_blocks < 0) return CSA2_E_INVALID_ARG;
@@ -200,6 +203,20 @@ csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_i
   if (op == CSA2_OP_INDEX_POOL && (!pool_mode || !ext_block_keys || !aligned(ext_block_keys, 4)))
     return CSA2_E_INVALID_ARG;
   if (op == CSA2_OP_INDEX_REINDEX && pool_mode && (!pool_in || !n_pool_in)) return CSA2_E_INVALID_ARG;
+  return CSA2_OK;
+}
+
+csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                        const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                        int32_t max_nvis, const uint32_t *ext_block_keys, const int32_t *pool_in,
+                        const int32_t *n_pool_in, int32_t k_blocks, int32_t k_pos,
+                        int32_t *pool_out, int32_t *n_pool_out, int32_t *topk, int32_t *n_topk,
+                        void *workspace, size_t workspace_bytes, void *stream_ptr) {
+  const csa2_status cs = check_indexer(op, cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis,
+                                       ext_block_keys, pool_in, n_pool_in, k_blocks, k_pos, pool_out,
+                                       n_pool_out, topk, n_topk);
+  if (cs != CSA2_OK) return cs;
+  const bool pool_mode = k_blocks > 0;
   const Layout L = plan_workspace(op, n_rows, max_nvis, k_blocks, k_pos);
   if (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
 
@@ -293,9 +310,56 @@ csa2_status run_records(bool to_records, const csa2_cache *cache, int32_t seq, i
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
 }
 
+// Scratch of csa2_index_full_noalloc: one array per device, in the library's
+// code object, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels and copies only ever
+// receive the device address that hipGetSymbolAddress returns for the
+// current device (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) on its first use.
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_status[dev] = (r == hipSuccess && p == nullptr) ? hipErrorInvalidSymbol : r;
+    g_scratch_ptr[dev] = g_scratch_status[dev] == hipSuccess ? p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_status[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+csa2_status csa2_index_full_noalloc(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                                    const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                                    int32_t max_nvis, int32_t k_blocks, int32_t k_pos,
+                                    int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
+                                    int32_t *n_topk, void *stream) {
+  const csa2_status cs = check_indexer(CSA2_OP_INDEX_FULL, cache, q_idx, w, row_seq, row_nvis, n_rows,
+                                       max_nvis, nullptr, nullptr, nullptr, k_blocks, k_pos, pool_blocks,
+                                       n_pool, topk, n_topk);
+  if (cs != CSA2_OK) return cs;
+  const size_t need = plan_workspace(CSA2_OP_INDEX_FULL, n_rows, max_nvis, k_blocks, k_pos).total;
+  if (need > (size_t)CSA2_NOALLOC_SCRATCH_BYTES) return CSA2_E_UNSUPPORTED;
+  void *ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return CSA2_E_HIP;
+  return run_indexer(CSA2_OP_INDEX_FULL, cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis,
+                     nullptr, nullptr, nullptr, k_blocks, k_pos, pool_blocks, n_pool, topk, n_topk,
+                     ws, (size_t)CSA2_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 csa2_status csa2_quantize_fp4(const float *x, int64_t n, int32_t dim, int32_t group,
                               const int64_t *dst_rows, uint8_t *codes, uint8_t *scales,

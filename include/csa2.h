@@ -27,10 +27,11 @@
  * Conventions for every call:
  *   - Every array argument is a DEVICE pointer owned by the caller (for
  *     example a torch tensor's storage); struct arguments are host pointers
- *     to structs that hold device pointers.  The library allocates no memory,
- *     keeps no pointer after it returns, and holds no mutable global state;
- *     scratch memory is the caller's `workspace`, sized by
- *     csa2_workspace_size().
+ *     to structs that hold device pointers.  The library allocates no memory
+ *     and keeps no pointer after it returns; scratch memory is the caller's
+ *     `workspace`, sized by csa2_workspace_size().  The one exception is
+ *     csa2_index_full_noalloc, whose scratch is a static per-device array
+ *     (its only global state is that array's address per device).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued on it; CSA2_OK means "validated and enqueued".  Device faults
  *     show up at the caller's next synchronisation.
@@ -208,6 +209,30 @@ csa2_status csa2_index_full(const csa2_cache *cache, const uint16_t *q_idx, cons
                             int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
                             int32_t *n_topk, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* csa2_index_full without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
+ * results and rules as csa2_index_full.  The scratch memory is a static
+ * array of CSA2_NOALLOC_SCRATCH_BYTES inside the library, one per device,
+ * held until the process ends; the current device's array is used (the
+ * stream must belong to the current device), and its address is looked up
+ * once per device on the first call there.  The call allocates nothing.
+ * The array keeps the last call's contents; no call depends on them.  Calls
+ * that overlap on one device (on different streams, or from different
+ * threads before the earlier one's kernels finished) share the array and
+ * race: order them on one stream.
+ * Returns CSA2_E_UNSUPPORTED when these sizes need more scratch than the
+ * array holds, i.e. csa2_workspace_size(CSA2_OP_INDEX_FULL, n_rows,
+ * max_nvis, k_blocks, k_pos) > CSA2_NOALLOC_SCRATCH_BYTES (16 MiB: enough
+ * for, e.g., 16 decode rows at 2^20 visible entries with 2,048 blocks and
+ * Top-512; flat mode needs 4 B per row and visible entry). */
+#define CSA2_NOALLOC_SCRATCH_BYTES (16u << 20)
+csa2_status csa2_index_full_noalloc(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
+                                    const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
+                                    int32_t max_nvis, int32_t k_blocks, int32_t k_pos,
+                                    int32_t *pool_blocks, int32_t *n_pool, int32_t *topk,
+                                    int32_t *n_topk, void *stream);
 
 /* S2 alone -- the scan stage of csa2_index_full in block mode, for callers
  * that schedule or time the context-proportional scan separately.  For each

@@ -84,6 +84,32 @@ def test_cache_append_validation():
     assert f(ctypes.byref(c), None, None, 0, None, None) == OK                 # nothing to do
 
 
+def test_index_full_noalloc_validation():
+    """The no-workspace variant checks its arguments like csa2_index_full and
+    rejects sizes whose scratch exceeds its static array, all before touching
+    the device."""
+    lib = csa2.load()
+    c = cache_struct(cap=1 << 20)
+    f = lib.csa2_index_full_noalloc
+
+    def call(R=8, max_nvis=1 << 20, kb=2048, kp=512, pool=FAKE, npool=FAKE, cache=None, q=FAKE):
+        return f(cache if cache is not None else ctypes.byref(c), q, FAKE, FAKE, FAKE, R, max_nvis,
+                 kb, kp, pool, npool, FAKE, FAKE, None)
+
+    assert call(max_nvis=(1 << 20) + 1) == INVALID          # beyond cap
+    assert call(R=0) == INVALID
+    assert call(kp=0) == INVALID
+    assert call(q=FAKE + 2) == INVALID
+    assert call(pool=None) == INVALID
+    assert call(kb=4097) == UNSUPPORTED
+    assert call(cache=ctypes.byref(cache_struct(null_ik=True))) == INVALID
+    # 8 decode rows at 2^20 entries fit in the static scratch; 4,096 flat rows do not
+    assert lib.csa2_workspace_size(1, 8, 1 << 20, 2048, 512) <= B.NOALLOC_SCRATCH_BYTES
+    assert lib.csa2_workspace_size(1, 4096, 32768, 0, 512) > B.NOALLOC_SCRATCH_BYTES
+    assert call(R=4096, max_nvis=32768, kb=0, pool=None, npool=None) == UNSUPPORTED
+    assert call(R=64, max_nvis=1 << 20) == UNSUPPORTED
+
+
 def test_index_validation():
     lib = csa2.load()
     c = cache_struct()
