@@ -479,7 +479,11 @@ def test_sparse_attn_global_fused_and_merge(csa2, H, split):
     (16, 1, 2048, 1024, True),    # 96 tiles over 48 work-groups: the merge's loop past 16 splits
     (64, 200, 64, 32, True),      # 200 rows: no split even with a workspace requested
     (16, 5, 33, 1, True),         # one-row window, a 1-key second tile
-], ids=["h32_ragged_split", "h32_ragged", "h16_2048_1024_48splits", "h64_200rows", "h16_tiny_tiles"])
+    (16, 100, 512, 128, True),    # 100 rows: a few splits per row
+    (32, 40, 300, 70, True),      # 32 heads x 40 rows: splits of two head groups
+    (16, 200, 200, 128, True),    # 200 rows of 16 heads: one work-group per row
+], ids=["h32_ragged_split", "h32_ragged", "h16_2048_1024_48splits", "h64_200rows", "h16_tiny_tiles",
+        "h16_100rows", "h32_40rows", "h16_200rows"])
 def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
     rng = np.random.default_rng(k_pos + window)
     n_vis = max(3000, k_pos + 10)
