@@ -154,11 +154,22 @@ attn_kernel(AttnArgs a) {
   int t_end = split ? t_begin + a.tiles_per_split : n_all;
   t_end = t_end < n_all ? t_end : n_all;
 
-  // Q operand: qa[t] = q[r][h0 + c][128G + 8t .. +7] in f16, t < 16 (the
-  // contraction over the 512 channels runs in this lane-consistent order)
+  // Q operand: qa[t] = 2^k q[r][h0 + c][128G + 8t .. +7] in f16, t < 16 (the
+  // contraction over the 512 channels runs in this lane-consistent order),
+  // with the power of two 2^k of head h0 + c (its largest |q| over the four
+  // lanes that hold it); sl = scale * log2(e) * 2^-k scales its logits back
   f16x8 qa[16];
+  float sl;
+  {
+    u16x2 m2 = {0, 0};
 #pragma unroll
-  for (int t = 0; t < 16; ++t) qa[t] = bf16x8_to_f16(q_raw[t]);
+    for (int t = 0; t < 16; ++t) m2 = bf16x8_absmax(q_raw[t], m2);
+    const int k = q_prescale_exp(umax_rows(absmax_bits(m2)));
+    const float up = exp2i(k);
+    sl = a.scale_log2 * exp2i(-k);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) qa[t] = bf16x8_to_f16_scaled(q_raw[t], up);
+  }
 
   // Accumulators, lane (G, c), block db: OT: O[head h0 + c][channels
   // 128w + 16db + 4G .. +3] (four consecutive channels of one head, stored
@@ -265,7 +276,7 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float x = (q0[i] + q1[i]) + (q2[i] + q3[i]);
-      sv[i] = ((vmask >> (4 * G + i)) & 1u) ? x * a.scale_log2 : -INFINITY;
+      sv[i] = ((vmask >> (4 * G + i)) & 1u) ? x * sl : -INFINITY;
       lmax = fmaxf(lmax, sv[i]);
     }
     lmax = fmaxf(lmax, swap_rows16(lmax));                       // lanes c, c + 16

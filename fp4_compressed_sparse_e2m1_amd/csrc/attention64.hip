@@ -16,7 +16,9 @@
 //         [128q, 128q + 128) of key block h2 of tile t, stores it in LDS
 //         (natural [key][channel] layout) and computes the partial logits
 //         S^T = K Q^T over that quarter for all 64 heads (16x16x32 MFMAs, Q
-//         held in registers); the partials go to LDS ([quarter][head][key]).
+//         held in registers, pre-scaled by a power of two per head and
+//         quarter that brings it into f16 range exactly); the partials, scaled
+//         back and times the softmax scale, go to LDS ([quarter][head][key]).
 //   B(t): online softmax (base 2) of heads 8w .. 8w + 7: lane l sums the four
 //         quarter partials of head 8w + l % 8 for keys 4 (l / 8) .. + 3 and
 //         writes the probabilities (f16) and the head's rescale factor.  The
@@ -223,14 +225,24 @@ attn_h64_kernel(AttnArgs a) {
     sl2.nid[kb] = n2[kb];
   }
 
-  // Q operand of the logits: qa[hb][t] = q[r][16hb + c][128q + 32G + 8t .. +7]
-  // in f16 (the contraction runs over the quarter in this lane-consistent
-  // order)
+  // Q operand of the logits: qa[hb][t] = 2^k q[r][16hb + c][128q + 32G + 8t
+  // .. +7] in f16 (the contraction runs over the quarter in this
+  // lane-consistent order), with a power of two 2^k per head and quarter (from
+  // the largest |q| of head 16hb + c in quarter q, over the four lanes that
+  // hold it).  The partial logits are scaled back on the way out, together
+  // with the softmax scale: sl[hb] = scale * log2(e) * 2^-k.
   f16x8 qa[4][4];
+  float sl[4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
+  for (int hb = 0; hb < 4; ++hb) {
+    u16x2 m2 = {0, 0};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qa[hb][t] = bf16x8_to_f16(q_raw[hb][t]);
+    for (int t = 0; t < 4; ++t) m2 = bf16x8_absmax(q_raw[hb][t], m2);
+    const int k = q_prescale_exp(umax_rows(absmax_bits(m2)));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[hb][t] = bf16x8_to_f16_scaled(q_raw[hb][t], exp2i(k));
+    sl[hb] = a.scale_log2 * exp2i(-k);
+  }
 
   // O^T accumulators: acc[hb][db] lane (G, c) holds
   // O[16hb + c][64w + 16db + 4G + i]
@@ -305,7 +317,7 @@ attn_h64_kernel(AttnArgs a) {
       for (int hb = 0; hb < 4; ++hb) sacc[hb] = mfma16x16x32(kf[i], qa[hb][i], sacc[hb]);
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
-      *reinterpret_cast<f32x4 *>(&s_part[q][16 * hb + c][16 * h2 + 4 * G]) = sacc[hb];
+      *reinterpret_cast<f32x4 *>(&s_part[q][16 * hb + c][16 * h2 + 4 * G]) = sacc[hb] * sl[hb];
   };
 
   // ---- B(T): online softmax of head hs over keys ks .. ks + 3 of tile T
@@ -318,7 +330,7 @@ attn_h64_kernel(AttnArgs a) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sv[j] = ((mask >> (ks + j)) & 1u) ? x[j] * a.scale_log2 : -INFINITY;
+      sv[j] = ((mask >> (ks + j)) & 1u) ? x[j] : -INFINITY;
       tmax = fmaxf(tmax, sv[j]);
     }
     // the eight lanes of head hs: l ^ 8, l ^ 16, l ^ 32

@@ -58,16 +58,48 @@ __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t byte) {
   return v[0];
 }
 
-// bf16 bit pattern -> fp16.  Exact for |v| in [2^-14, 65504] (normal fp16);
-// smaller magnitudes round to the fp16 subnormal grid (2^-24 spacing).
-__device__ __forceinline__ _Float16 bf16_to_f16(uint16_t b) {
-  return (_Float16)__uint_as_float((uint32_t)b << 16);
+// Q enters the f16 contractions (logits, index scores) times a power of two
+// 2^k per head, chosen from the head's largest bf16 magnitude so that it lands
+// in [2^15, 2^16): no value overflows f16, every value at least 2^-29 times
+// the head's largest is an f16 normal and converts exactly (8 significant
+// bits), smaller ones round toward zero on the f16 subnormal grid, and the f32
+// results are scaled back by 2^-k exactly.  k is at most 100 (a head whose
+// largest |q| is below 2^-85 keeps a smaller factor), so 2^-k times a softmax
+// scale or an index weight stays a normal f32.
+
+// Running maximum of the magnitude bits (sign cleared, so they order as the
+// magnitudes) of eight bf16 values, two lanes of 16 bits.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 bf16x8_absmax(uint4 v, u16x2 m) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  return m;
+}
+__device__ __forceinline__ uint32_t absmax_bits(u16x2 m) { return m[0] > m[1] ? m[0] : m[1]; }
+
+// the exponent k for a head whose largest magnitude bits are mx
+__device__ __forceinline__ int q_prescale_exp(uint32_t mx) {
+  const int k = 142 - (int)(mx >> 7);     // 142: the biased exponent of 2^15
+  return k < 100 ? k : 100;
 }
 
-__device__ __forceinline__ f16x8 bf16x8_to_f16(uint4 v) {
-  return f16x8{bf16_to_f16(v.x & 0xFFFF), bf16_to_f16(v.x >> 16), bf16_to_f16(v.y & 0xFFFF),
-               bf16_to_f16(v.y >> 16),    bf16_to_f16(v.z & 0xFFFF), bf16_to_f16(v.z >> 16),
-               bf16_to_f16(v.w & 0xFFFF), bf16_to_f16(v.w >> 16)};
+// 2^k as a float, -126 <= k <= 127
+__device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// eight bf16 values times up (a power of two) in f16; exact whenever the
+// products are f16 normals
+__device__ __forceinline__ f16x8 bf16x8_to_f16_scaled(uint4 v, float up) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  f16x8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 pr = __builtin_bit_cast(
+        f16x2, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[i] << 16) * up, __uint_as_float(w[i] & 0xFFFF0000u) * up));
+    h[2 * i] = pr[0];
+    h[2 * i + 1] = pr[1];
+  }
+  return h;
 }
 
 // max(x, 0) in one instruction: median of x, 0 and the largest float (+inf
@@ -99,6 +131,15 @@ __device__ __forceinline__ float max8(float m) {
 // (ds_swizzle in bit-mask mode: and 0x1F, or 0, xor 0x10; no LDS memory).
 __device__ __forceinline__ float swap_rows16(float x) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48, in each of them.
+__device__ __forceinline__ uint32_t umax_rows(uint32_t x) {
+  const uint32_t o16 = (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+  x = x > o16 ? x : o16;
+  const auto sw = __builtin_amdgcn_permlane32_swap((int)x, (int)x, false, false);
+  const uint32_t o32 = (uint32_t)((__lane_id() & 32) ? sw[0] : sw[1]);
+  return x > o32 ? x : o32;
 }
 
 // Maximum of unsigned keys over each aligned group of 8 lanes, in every lane

@@ -88,21 +88,31 @@ score_kernel(ScoreArgs a) {
   const int64_t chunk0 = (int64_t)chunk_id * kChunk;
   if (chunk0 >= n_slots) return;
 
-  // Query operand: lane (G, c) holds head c's channels 32G + 8t .. +7, t = 0..3.
-  f16x8 qa[4];
+  // Query operand: lane (G, c) holds head c's channels 32G + 8t .. +7, t = 0..3,
+  // times the head's power of two 2^k (from its largest |q| over the four
+  // lanes that hold it); relu commutes with the positive factor, so each
+  // head's weight takes 2^-k instead.
+  uint4 qr[4] = {};
   if (c < 8) {
     const uint4 *qp = reinterpret_cast<const uint4 *>(a.q_idx + ((int64_t)r * 8 + c) * 128 + 32 * G);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qa[t] = bf16x8_to_f16(qp[t]);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) qa[t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = 0; t < 4; ++t) qr[t] = qp[t];
   }
+  u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) m2 = bf16x8_absmax(qr[t], m2);
+  const int kq = q_prescale_exp(umax_rows(absmax_bits(m2)));
+  f16x8 qa[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) qa[t] = bf16x8_to_f16_scaled(qr[t], exp2i(kq));
   float wh[4] = {0.f, 0.f, 0.f, 0.f};
   if (G < 2) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) wh[i] = a.w[(int64_t)r * 8 + 4 * G + i];
   }
+  // the weight of head 4G + i takes the exponent held by lane 4G + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wh[i] *= exp2i(-__builtin_amdgcn_ds_bpermute(4 * (4 * G + i), kq));
 
   const uint8_t *codes_base = a.ik_codes + (int64_t)seq * a.cap * 64;
   const uint8_t *scales_base = a.ik_scales + (int64_t)seq * a.cap * 4;
@@ -253,19 +263,30 @@ score_rows_kernel(ScoreArgs a, int32_t n_rows) {
   // 4(G & 1) .. +3 of row 2p + (G >> 1), entry c.
   float wh[RP][4];
 #pragma unroll
+  // Each (row, head) enters with its power of two 2^k (from its largest |q|
+  // over the four lanes that hold it) and its weight takes 2^-k: the weight
+  // of lane (G, c)'s output head 4 (G & 1) + i of row 2p + (G >> 1) takes the
+  // exponent of lane 4G + i, which holds that head.
   for (int p = 0; p < RP; ++p) {
     const int rq = r0 + 2 * p + (c >> 3);
+    uint4 qr[4] = {};
     if (rq < n_rows) {
       const uint4 *qp = reinterpret_cast<const uint4 *>(a.q_idx + ((int64_t)rq * 8 + (c & 7)) * 128 + 32 * G);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) qa[p][t] = bf16x8_to_f16(qp[t]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) qa[p][t] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < 4; ++t) qr[t] = qp[t];
     }
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m2 = bf16x8_absmax(qr[t], m2);
+    const int kq = q_prescale_exp(umax_rows(absmax_bits(m2)));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[p][t] = bf16x8_to_f16_scaled(qr[t], exp2i(kq));
     const int rw = r0 + 2 * p + (G >> 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wh[p][i] = rw < n_rows ? a.w[(int64_t)rw * 8 + 4 * (G & 1) + i] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const float wv = rw < n_rows ? a.w[(int64_t)rw * 8 + 4 * (G & 1) + i] : 0.f;
+      wh[p][i] = wv * exp2i(-__builtin_amdgcn_ds_bpermute(4 * (4 * G + i), kq));
+    }
   }
 
   while (pending) {

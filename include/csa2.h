@@ -47,6 +47,13 @@
  *   - Results are deterministic: fixed reduction orders, Top-K lists sorted
  *     ascending.
  *   - NaN or infinite inputs are outside the contract.
+ *   - Q and q_idx may hold any finite bf16 values.  Each head enters the f16
+ *     contractions times a power of two 2^k that puts its largest |q| in
+ *     [2^15, 2^16), and the f32 results are scaled back by 2^-k, so every
+ *     value at least 2^-29 times the head's largest converts exactly (smaller
+ *     ones round on the f16 subnormal grid; k is capped at 100, so a head
+ *     whose largest |q| is below 2^-85 keeps a smaller factor).  The scaled
+ *     logits (scale * q.k) and the index scores must be finite in fp32.
  *
  * Data layout in HBM (one plane per field, struct-of-arrays):
  *   kv_codes  [n_seq][cap][256] uint8   main latent, 512 E2M1 codes

@@ -419,12 +419,19 @@ def attn_case(csa2, H, n_vis_list, topk_rows, swa_ends, seed=0, swa_len=200, win
                 swa_end=np.asarray(swa_ends, np.int32), window=window, H=H)
 
 
-def oracle_attn(c, r):
+def oracle_attn(c, r, q=None, scale=SCALE):
     s = int(c["row_seq"][r])
     kvc, kvs, _, _ = c["ora"][s]
     end = int(min(max(c["swa_end"][r], 0), c["swa"].shape[1]))
     rows = c["swa"][s, max(0, end - c["window"]):end].numpy()
-    return oracle.attend_row(W.bf16_bits(c["q"][r]), kvc, kvs, c["topk"][r][:c["ntopk"][r]], rows, SCALE)
+    q = c["q"] if q is None else q
+    return oracle.attend_row(W.bf16_bits(q[r]), kvc, kvs, c["topk"][r][:c["ntopk"][r]], rows, scale)
+
+
+def pow2_bf16(x, e):
+    """bf16 tensor x times 2^e (e broadcast against x), exact while the
+    results stay bf16 normals."""
+    return (x.double() * torch.pow(2.0, torch.as_tensor(e, dtype=torch.float64))).to(torch.bfloat16)
 
 
 @pytest.mark.parametrize("split", [False, True], ids=["one_wg_per_row", "split_rows"])
@@ -520,18 +527,94 @@ def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
                     np.stack([x["lse"] for x in refs]), f"H{H} k{k_pos} w{window} merged")
 
 
+@pytest.mark.parametrize("H", [16, 64])
 @pytest.mark.parametrize("split", [False, True])
-def test_attention_empty_everything(csa2, split):
+def test_attention_empty_everything(csa2, split, H):
     rows = [(np.array([], np.int64), 0), (np.array([-1, -1], np.int64), 0)]
-    c = attn_case(csa2, 16, [100], rows, swa_ends=[0, -5], seed=3)
-    o = torch.full((2, 16, 512), 5.0, device="cuda")
-    lse = torch.zeros((2, 16), device="cuda")
+    c = attn_case(csa2, H, [100], rows, swa_ends=[0, -5], seed=3)
+    o = torch.full((2, H, 512), 5.0, device="cuda")
+    lse = torch.zeros((2, H), device="cuda")
     swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), 128)
-    ws = csa2.attn_workspace(2, 16, c["topk"].shape[1], 128) if split else None
+    ws = csa2.attn_workspace(2, H, c["topk"].shape[1], 128) if split else None
     csa2.csa2_sparse_attn(c["cache"], dev(c["q"]), dev(c["row_seq"]), dev(c["topk"]),
                           dev(c["ntopk"]), SCALE, o, lse, swa=swa, workspace=ws)
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["one_wg_per_row", "split_rows"])
+@pytest.mark.parametrize("H", [16, 64])
+def test_attention_q_range(csa2, H, split):
+    """Q anywhere in the finite bf16 range.  (a) q * 2^e with the softmax
+    scale times 2^-e has the same logits, for e from -80 (a head's largest
+    |q| near 2^-78) to 120 (near the largest finite bf16); (b) the heads of
+    one row 2^-80 .. 2^60 apart, so flat and one-hot softmaxes sit side by
+    side.  Against the oracle on the very same inputs."""
+    rng = np.random.default_rng(11 + H)
+    rows = [(np.sort(rng.choice(3000, 300, replace=False)), 0),
+            (np.sort(rng.choice(3000, 77, replace=False)), 0)]
+    c = attn_case(csa2, H, [3000], rows, swa_ends=[200, 90], seed=31 + H)
+    R, k_pos = len(rows), c["topk"].shape[1]
+    swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), c["window"])
+    ws = csa2.attn_workspace(R, H, k_pos, c["window"]) if split else None
+    if split:
+        assert ws is not None
+
+    def check(q, scale, what):
+        o = torch.empty((R, H, 512), device="cuda")
+        lse = torch.empty((R, H), device="cuda")
+        csa2.csa2_sparse_attn(c["cache"], dev(q), dev(c["row_seq"]), dev(c["topk"]), dev(c["ntopk"]),
+                              scale, o, lse, swa=swa, workspace=ws)
+        torch.cuda.synchronize()
+        refs = [oracle_attn(c, r, q, scale) for r in range(R)]
+        check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o"] for x in refs]),
+                        np.stack([x["lse"] for x in refs]), what)
+
+    for e in (-80, -30, 40, 120):
+        q = pow2_bf16(c["q"], e)
+        assert torch.all(torch.isfinite(q.float()))
+        check(q, SCALE * 2.0 ** -e, f"q * 2^{e}")
+    e_head = np.array([-80, -40, 0, 30, 60])[np.arange(H) % 5]
+    check(pow2_bf16(c["q"], e_head[None, :, None]), SCALE, "heads 2^-80 .. 2^60")
+
+
+@pytest.mark.parametrize("shape", ["rows_one_per_wg", "many_rows_flat", "many_rows_block"])
+def test_index_q_range(csa2, shape):
+    """q_idx anywhere in the finite bf16 range: a row's (or one head's) q_idx
+    times 2^e with its weight times 2^-e, for e from -80 to 120, and a row
+    whose eight heads lie 2^-80 .. 2^110 apart.  The selection must match the
+    oracle's on the very same inputs (the scores stay of order one, so the
+    tie tolerance is meaningful).  Rows of distinct sequences are scored one
+    per work-group, many rows of one sequence by the many-row kernel."""
+    n = 4096
+    cache, ora = make_index_case(csa2, [n], n, seed=61)
+    exps = [-80, -30, 0, 30, 90, 120]
+    mixed = [-80, -50, -20, 0, 20, 50, 80, 110]
+    if shape == "rows_one_per_wg":
+        R, k_blk = 7, 64
+        nvis = [n, n - 5, 3000, n, 1000, n, n - 1]
+    else:
+        R, k_blk = 16, (0 if shape == "many_rows_flat" else 64)
+        nvis = [n - 15 + r for r in range(R)]
+    E = np.array([[exps[r % len(exps)]] * 8 for r in range(R)], np.float64)
+    E[R - 1] = mixed
+    if R > 8:
+        E[5] = mixed[::-1]
+    qidx = pow2_bf16(W.bf16_normal((R, 8, 128), seed=62), E[:, :, None])
+    assert torch.all(torch.isfinite(qidx.float()))
+    w = (W.uniform01((R, 8), seed=63).double() * torch.from_numpy(np.power(2.0, -E))).float()
+    k_pos = 512
+    qd, wd = dev(qidx), dev(w)
+    pool, npool, topk, ntopk = run_full(csa2, cache, qd, wd, [0] * R, nvis, max(nvis), k_blk, k_pos)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    _, _, ikc, iks = ora[0]
+    for r in range(R):
+        ref = oracle.full_layer_select(qb[r], wn[r], ikc, iks, nvis[r], k_blk, k_pos)
+        if k_blk:
+            check_full_row(csa2, cache, qd[r:r + 1], wd[r:r + 1], 0, nvis[r], pool[r], npool[r], topk[r],
+                           ntopk[r], ref, k_blk, k_pos, f"row {r} e {E[r].tolist()}")
+        else:
+            check_topk(topk[r], ntopk[r], ref, f"row {r} e {E[r].tolist()}")
 
 
 # ------------------------------------------------------------- one layer e2e
