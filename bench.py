@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -530,7 +531,7 @@ def decode_b32(steps, warmup):
     c = build(wid=2)
     wall, scan_ms, per_layer = run_gpu(c, steps, warmup, True)
     B, T, L = c["B"], c["T"], c["L"]
-    scan_bytes = IK_BYTES * T * B + BLOCK_KEY_BYTES * ((T + 7) // 8) * B
+    scan_bytes = IK_BYTES * T * B                  # key reads (68 B per visible entry)
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     modes = c["wl"].layers
     mode_us = {m: 1e3 * sum(t for t, mm in zip(per_layer, modes) if mm == m) /
@@ -565,8 +566,8 @@ def multi_query_scan(c, q_per_seq=4, steps=20, warmup=3):
     each of the 8 sequences checks q_per_seq queries at once (draft tokens,
     n_vis = T - q_per_seq + 1 .. T), so 8 x q_per_seq query rows, laid out
     sequence by sequence, share each indexer key read.  Algorithmic bytes:
-    every visible key read once per sequence (68 B per entry) + one 4-B block
-    key per block of 8 per row."""
+    every visible key read once per sequence (68 B per entry); the 4-B block
+    keys written per block of 8 and row are workspace traffic, not counted."""
     import torch
 
     import workloads as W
@@ -593,7 +594,7 @@ def multi_query_scan(c, q_per_seq=4, steps=20, warmup=3):
         b.record()
     torch.cuda.synchronize()
     us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / steps
-    byt = IK_BYTES * T * B + BLOCK_KEY_BYTES * ((T + 7) // 8) * R
+    byt = IK_BYTES * T * B                         # key reads (68 B per visible entry)
     achieved = byt / (us * 1e-6) / 1e9
     return {"queries_per_sequence": q_per_seq, "rows": R, "avg_launch_us": round(us, 2),
             "query_tokens_per_s": round(R / (us * 1e-6), 1),
@@ -740,11 +741,37 @@ def cpu_baseline(c, rows):
     t0 = time.perf_counter()
     oracle.parallel_map(full_step, list(range(rows)), rows)
     dt = time.perf_counter() - t0
+    # the same oracle on one row and one thread
+    t0 = time.perf_counter()
+    full_step(0)
+    dt1 = time.perf_counter() - t0
     return {"value": rows * c["L"] / dt, "unit": "query-tokens/s per CSA2 layer", "cores": rows,
             "kind": "oracle",
+            "value_1thread": c["L"] / dt1,
+            "host_cores": host_cores(), "cpu_model": cpu_model(),
             "sample": f"{rows} of the {B} query rows of the 1M-context decode step, all {c['L']} layers "
                       f"(scan of {T} entries, pool, Top-512, 4 re-indexes, 20 attentions with SWA), "
-                      f"one host thread per row; {dt:.1f} s wall"}
+                      f"one host thread per row; {dt:.1f} s wall; value_1thread: row 0 alone on one "
+                      f"thread, {dt1:.1f} s"}
+
+
+def host_cores():
+    """Host CPUs this process may run on (its affinity mask)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or None
 
 
 def main():
@@ -783,9 +810,10 @@ def main():
     B, T, L = c["B"], c["T"], c["L"]
     ms_step = wall * 1e3 / args.steps
     value = B * L / (wall / args.steps)
-    # algorithmic bytes of one scan launch: every entry's indexer key read
-    # once, one block key written per 8 entries
-    scan_bytes = IK_BYTES * T * B + BLOCK_KEY_BYTES * ((T + 7) // 8) * B
+    # algorithmic bytes of one scan launch: every entry's 68-B indexer key read
+    # once (the 4-B block keys it writes per 8 entries are workspace traffic,
+    # reported beside it, not counted)
+    scan_bytes = IK_BYTES * T * B
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     modes = c["wl"].layers
     mode_us = {m: 1e3 * sum(t for t, mm in zip(per_layer, modes) if mm == m) /
@@ -811,7 +839,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "score_kernel<block max> (csa2_index_scan)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic_bytes(),
-                     "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(scan_ms * 1e3, 2)},
+                     "algorithmic_bytes_per_launch": scan_bytes,
+                     "block_key_bytes_written": BLOCK_KEY_BYTES * ((T + 7) // 8) * B,
+                     "avg_launch_us": round(scan_ms * 1e3, 2)},
         "per_layer_us_eager": {k: round(v, 2) for k, v in mode_us.items()},
         "full_layer_query_tokens_per_s": round(B / (mode_us["full"] * 1e-6), 1),
         "build_s": round(t_build, 1),

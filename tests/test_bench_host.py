@@ -40,3 +40,9 @@ def test_pages_figures_from_the_cache_layout():
     assert f["bytes_per_token_at_2_5_entries"]["csa2_amd"] == 890
     assert f["kernels_per_reuse_layer_decode"]["csa2_amd"] == 2     # attention + split merge at batch 8
     assert abs(f["decode_flops_1m_over_4k"]["csa2_amd"] - 2_734_686_208 / 469_762_048) < 1e-3
+
+
+def test_host_description():
+    assert bench.host_cores() >= 1
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
