@@ -256,6 +256,56 @@ def capture(c):
     return graphs
 
 
+def launches_per_layer(c):
+    """Launches of each layer mode of the step, counted as the kernel nodes
+    of one HIP graph per layer (the Full layer's with its append and scan);
+    nodes of other kinds (copies, fills) are counted apart."""
+    import ctypes
+
+    import torch
+
+    hip = ctypes.CDLL("libamdhip64.so.7")    # the runtime torch already loaded
+
+    def count(fn):
+        g = torch.cuda.CUDAGraph(keep_graph=True)
+        with torch.cuda.graph(g):
+            fn()
+        h = ctypes.c_void_p(g.raw_cuda_graph())
+        n = ctypes.c_size_t(0)
+        if hip.hipGraphGetNodes(h, None, ctypes.byref(n)) != 0:
+            raise RuntimeError("hipGraphGetNodes failed")
+        nodes = (ctypes.c_void_p * max(1, n.value))()
+        if hip.hipGraphGetNodes(h, nodes, ctypes.byref(n)) != 0:
+            raise RuntimeError("hipGraphGetNodes failed")
+        kernels = 0
+        for i in range(n.value):
+            t = ctypes.c_int(-1)
+            if hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) != 0:
+                raise RuntimeError("hipGraphNodeGetType failed")
+            kernels += t.value == 0              # hipGraphNodeTypeKernel
+        del g
+        return kernels, n.value - kernels
+
+    layers = c["wl"].layers
+    full = layers.index("full")
+    out = {}
+    for l, mode in enumerate(layers):
+        if mode in out:
+            continue
+        if mode == "full":
+            def fn(l=l):
+                _append(c)
+                _scan(c, l)
+                _layer_tail(c, l, "full", None)
+        else:
+            def fn(l=l, mode=mode):
+                _layer_tail(c, l, mode, full)
+        k, other = count(fn)
+        out[mode] = {"kernels": k, "other_nodes": other}
+    torch.cuda.synchronize()
+    return out
+
+
 def _outputs(c):
     """Copies of what a step writes: the selections of the Full and Reindex
     layers, the pool, and the last layer's attention output."""
@@ -615,21 +665,23 @@ def path_flops_per_query(T, wl):
             + len(wl.layers) * 2 * 2 * wl.heads * 512 * keys)
 
 
-def pages_figures(c, step_ms_1m=None, step_ms_4k=None):
+def pages_figures(c, step_ms_1m=None, step_ms_4k=None, launches=None):
     """The pages' own figures (no hardware stated for any) beside what this
     library's layout and launch plan give, and the measured step-time ratio
     of the same 20-layer decode stack at 1M and at 4K context when given."""
     csa2, wl = c["csa2"], c["wl"]
     per_entry = c["cache"].nbytes // (c["B"] * c["T"])
     split = csa2.csa2_attn_workspace_size(c["B"], c["H"], wl.k_pos, wl.swa) > 0
+    reuse = launches["reuse"]["kernels"] if launches else (2 if split else 1)
     return {
         "bytes_per_entry": {"csa2_amd": per_entry, "pages": 356},
         "bytes_per_token_at_2_5_entries": {"csa2_amd": per_entry * 2.5, "pages": 890},
         "kernels_per_reuse_layer_decode": {
-            "csa2_amd": 2 if split else 1,
+            "csa2_amd": reuse,
             "pages": 11,
-            "note": "ours: sparse attention with the SWA branch fused (+ the split merge at this batch); "
-                    "the pages count the whole fused layer"},
+            "note": "ours (counted in the step's graph when launches_per_layer is present): sparse "
+                    "attention with the SWA branch fused (+ the split merge at this batch); the pages "
+                    "count the whole fused layer"},
         "kernels_per_reuse_layer_prefill": {
             "csa2_amd": 1 if csa2.csa2_attn_workspace_size(4096, c["H"], wl.k_pos, wl.swa) == 0 else 2,
             "pages": 15,
@@ -858,7 +910,8 @@ def main():
         wall4k, _, _ = run_gpu(c4k, args.steps, args.warmup, True)
         del c4k
         ms_4k = wall4k * 1e3 / args.steps
-    line["pages_figures"] = pages_figures(c, ms_step, ms_4k)
+    line["launches_per_layer"] = launches_per_layer(c)
+    line["pages_figures"] = pages_figures(c, ms_step, ms_4k, line["launches_per_layer"])
     line["hbm_copy_GBs"] = copy_bandwidth()
     if not args.no_attention_roofline:
         line["attention_b256_h64"] = reuse_attention(20, 3)

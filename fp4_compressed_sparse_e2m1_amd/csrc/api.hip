@@ -45,6 +45,22 @@ size_t select_scratch(int32_t rows, int64_t n_max, int k) {
   return (size_t)rows * (size_t)chunks[0] * (size_t)k * 8;
 }
 
+// Flat mode (every visible entry a candidate) scores and selects its rows in
+// passes of at most this many bytes of entry keys and selection scratch, so
+// its workspace is bounded by this size (or one row's need) however many
+// rows a call has.
+constexpr size_t kFlatPassBytes = (size_t)256 << 20;
+
+// Rows per flat-mode pass: as many as fit kFlatPassBytes (whole groups of 8,
+// the many-row scoring kernel's group), at least one.
+int32_t flat_pass_rows(int32_t n_rows, int32_t max_nvis, int32_t k_pos) {
+  const size_t per_row = round_up((size_t)(max_nvis > 0 ? max_nvis : 1) * 4) + 2 * select_scratch(1, max_nvis, k_pos);
+  int64_t rb = (int64_t)(kFlatPassBytes / per_row);
+  if (rb >= 8) rb -= rb % 8;
+  rb = rb < 1 ? 1 : rb;
+  return (int32_t)(rb < n_rows ? rb : n_rows);
+}
+
 struct Layout {
   size_t keys_a = 0;    // block keys or flat entry keys
   size_t keys_b = 0;    // pool candidate keys
@@ -72,9 +88,10 @@ Layout plan_workspace(int32_t op, int32_t rows, int32_t max_nvis, int32_t k_bloc
     const size_t h2 = select_scratch(rows, (int64_t)k_blocks * 8, k_pos);
     half = half > h2 ? half : h2;
   } else {
+    const int32_t rb = flat_pass_rows(rows, max_nvis, k_pos);
     L.keys_a = off;
-    off += round_up((size_t)rows * (size_t)(max_nvis > 0 ? max_nvis : 1) * 4);
-    half = select_scratch(rows, max_nvis, k_pos);
+    off += round_up((size_t)rb * (size_t)(max_nvis > 0 ? max_nvis : 1) * 4);
+    half = select_scratch(rb, max_nvis, k_pos);
   }
   half = round_up(half);
   L.half = half;
@@ -226,15 +243,27 @@ csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_i
   hipError_t e = hipSuccess;
 
   if (!pool_mode) {
-    // flat: every visible entry is a candidate
+    // flat: every visible entry is a candidate; the rows go in passes that
+    // fit the bounded workspace (one pass unless the rows are many)
+    const int32_t rb = flat_pass_rows(n_rows, max_nvis, k_pos);
     sa.keys_out = reinterpret_cast<uint32_t *>(ws + L.keys_a);
     sa.out_stride = max_nvis > 0 ? max_nvis : 1;
-    e = launch_score(kScoreFlat, sa, n_rows, max_nvis, stream);
-    if (e != hipSuccess) return CSA2_E_HIP;
-    SelectOut fin = {topk, n_topk, kMapId, nullptr, nullptr, 0};
-    e = run_select(sa.keys_out, sa.out_stride, kCountNvis, 0, max_nvis, k_pos, row_seq, row_nvis,
-                   cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half, n_rows, stream);
-    return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+    for (int32_t r0 = 0; r0 < n_rows; r0 += rb) {
+      const int32_t nr = n_rows - r0 < rb ? n_rows - r0 : rb;
+      ScoreArgs sp = sa;
+      sp.q_idx = q_idx + (int64_t)r0 * 8 * 128;
+      sp.w = w + (int64_t)r0 * 8;
+      sp.row_seq = row_seq + r0;
+      sp.row_nvis = row_nvis + r0;
+      e = launch_score(kScoreFlat, sp, nr, max_nvis, stream);
+      if (e != hipSuccess) return CSA2_E_HIP;
+      SelectOut fin = {topk + (int64_t)r0 * k_pos, n_topk + r0, kMapId, nullptr, nullptr, 0};
+      e = run_select(sp.keys_out, sp.out_stride, kCountNvis, 0, max_nvis, k_pos, row_seq + r0,
+                     row_nvis + r0, cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half, nr,
+                     stream);
+      if (e != hipSuccess) return CSA2_E_HIP;
+    }
+    return CSA2_OK;
   }
 
   const int32_t *pool = pool_in;

@@ -177,7 +177,10 @@ csa2_status csa2_cache_import(const csa2_cache *cache, int32_t seq, int64_t firs
 /* Scratch bytes that csa2_index_full (op CSA2_OP_INDEX_FULL),
  * csa2_index_reindex (op CSA2_OP_INDEX_REINDEX) or csa2_index_pool (op
  * CSA2_OP_INDEX_POOL) needs for these sizes; k_blocks = 0 selects flat mode
- * (not valid for CSA2_OP_INDEX_POOL).  Returns 0 for invalid arguments. */
+ * (not valid for CSA2_OP_INDEX_POOL).  Flat mode scores and selects its rows
+ * in passes of at most 256 MiB of scratch, so its size stays below that
+ * bound (or one row's own need, 4 B per visible entry plus selection
+ * scratch) however many rows a call has.  Returns 0 for invalid arguments. */
 size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,
                            int32_t k_pos);
 

@@ -186,6 +186,9 @@ def test_attention_validation():
     assert m(FAKE, 20, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == UNSUPPORTED
     assert m(FAKE, 16, FAKE, 0, ctypes.byref(good_swa), 1, 0.04, FAKE, FAKE, None, 0, None) == OK
     assert m(FAKE, 16, FAKE, 4, ctypes.byref(good_swa), 1, 0.04, FAKE + 8, FAKE, None, 0, None) == INVALID
+    # flat mode's workspace is bounded (rows go in passes)
+    assert lib.csa2_workspace_size(1, 4096, 32768, 0, 512) <= 256 << 20
+    assert lib.csa2_workspace_size(1, 1, 32768, 0, 512) >= 32768 * 4
     # a split needs its workspace: given but too small is an error, NULL is not
     ws = lib.csa2_attn_workspace_size(8, 64, 512, 128)
     assert ws >= 8 * 2 * 64 * 514 * 4

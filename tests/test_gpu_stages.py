@@ -229,6 +229,27 @@ def test_index_full_flat_mode(csa2, n_vis_rows):
         check_topk(topk[r], ntopk[r], ref, "flat")
 
 
+def test_index_flat_rows_in_passes(csa2):
+    """Flat mode with more rows than one 256-MiB pass holds (433 rows of up to
+    140,001 entries: 416 rows per pass): the workspace stays bounded and the
+    rows on both sides of the pass boundary match the oracle."""
+    n, R = 140001, 433
+    cache, ora = make_index_case(csa2, [n], n, seed=47)
+    nvis = [n - (R - 1 - r) for r in range(R)]
+    need = csa2.csa2_workspace_size(csa2.CSA2_OP_INDEX_FULL, R, n, 0, 512)
+    # (one pass of every row would need 4 B per entry and two 9-chunk
+    # selection buffers per row)
+    assert need <= 256 << 20 < R * (n * 4 + 2 * 9 * 512 * 8)
+    qidx = W.bf16_normal((R, 8, 128), seed=48)
+    w = W.uniform01((R, 8), seed=49)
+    _, _, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [0] * R, nvis, n, 0, 512)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    _, _, ikc, iks = ora[0]
+    for r in (0, 415, 416, R - 1):
+        ref = oracle.full_layer_select(qb[r], wn[r], ikc, iks, nvis[r], 0, 512)
+        check_topk(topk[r], ntopk[r], ref, f"row {r}")
+
+
 def test_index_flat_many_rows(csa2):
     """Flat scoring of many rows at once (the prefill shape: consecutive query
     tokens of one sequence, n_vis growing by one per row), with work-groups
@@ -481,16 +502,21 @@ def test_sparse_attn_global_fused_and_merge(csa2, H, split):
 
 
 @pytest.mark.parametrize("H,n_rows,k_pos,window,split", [
-    (32, 3, 97, 100, True),       # 32 heads; Top-K and window not multiples of the 32-key tile
+    (32, 3, 97, 100, True),       # 32 heads; Top-K and window not multiples of the tile
+    (32, 3, 1000, 100, True),     # the same with a long Top-K list
     (32, 3, 97, 100, False),
     (16, 1, 2048, 1024, True),    # 96 tiles over 48 work-groups: the merge's loop past 16 splits
     (64, 200, 64, 32, True),      # 200 rows: no split even with a workspace requested
     (16, 5, 33, 1, True),         # one-row window, a 1-key second tile
+    (16, 5, 1100, 1, True),       # a long Top-K list, a one-row window
     (16, 100, 512, 128, True),    # 100 rows: a few splits per row
     (32, 40, 300, 70, True),      # 32 heads x 40 rows: splits of two head groups
     (16, 200, 200, 128, True),    # 200 rows of 16 heads: one work-group per row
-], ids=["h32_ragged_split", "h32_ragged", "h16_2048_1024_48splits", "h64_200rows", "h16_tiny_tiles",
-        "h16_100rows", "h32_40rows", "h16_200rows"])
+    (16, 300, 200, 128, False),   # 300 rows, an odd number of Top-K tiles per row
+    (32, 130, 97, 100, True),     # 32 heads x 130 rows, split
+], ids=["h32_ragged_split", "h32_long_split", "h32_ragged", "h16_2048_1024_48splits", "h64_200rows",
+        "h16_tiny_tiles", "h16_long_tiny_window", "h16_100rows", "h32_40rows", "h16_200rows", "h16_300rows",
+        "h32_130rows"])
 def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
     rng = np.random.default_rng(k_pos + window)
     n_vis = max(3000, k_pos + 10)
