@@ -392,12 +392,26 @@ score_rows_kernel(ScoreArgs a, int32_t n_rows) {
       uint4 ca[U], cb[U];
       uint32_t sa_[U], sb[U];
       load(0, ca, sa_);
-      for (int tb = 0; tb < n_tiles; tb += 2 * U) {
-        if (tb + U < n_tiles) load(tb + U, cb, sb);
-        compute(tb, ca, sa_);
-        if (tb + U >= n_tiles) break;
-        if (tb + 2 * U < n_tiles) load(tb + 2 * U, ca, sa_);
-        compute(tb + U, cb, sb);
+      if constexpr (FULL) {
+        // a whole chunk: every pass issues the same loads (the last one
+        // re-reads its own second batch), so no load is conditional and each
+        // wait names exactly the batch it needs
+        static_assert(kTilesPerWave % (2 * U) == 0, "whole passes per chunk");
+#pragma unroll 1
+        for (int tb = 0; tb < kTilesPerWave; tb += 2 * U) {
+          load(tb + U, cb, sb);
+          compute(tb, ca, sa_);
+          load(tb + 2 * U < kTilesPerWave ? tb + 2 * U : tb + U, ca, sa_);
+          compute(tb + U, cb, sb);
+        }
+      } else {
+        for (int tb = 0; tb < n_tiles; tb += 2 * U) {
+          if (tb + U < n_tiles) load(tb + U, cb, sb);
+          compute(tb, ca, sa_);
+          if (tb + U >= n_tiles) break;
+          if (tb + 2 * U < n_tiles) load(tb + 2 * U, ca, sa_);
+          compute(tb + U, cb, sb);
+        }
       }
     };
     if (chunk0 + kScoreRowsChunk <= nmin)
