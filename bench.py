@@ -50,9 +50,9 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "7c39adcb03dd80f7366099ff6f11d84eb8663420dd902e5bea7be11cb367c653",
-    "fetch_kib": 278658.448, "fetch_scale": 524288 / 262165.5625,
-    "write_kib": 4096.771, "write_scale": 524288 / 524288.0,
+    "sha256": "2a0dfe19e124227aa6d4f3de514ede93d3c96a254524bf6c910fe07b85dc38b8",
+    "fetch_kib": 278659.698, "fetch_scale": 524288 / 262166.625,
+    "write_kib": 4096.484, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -63,9 +63,9 @@ ATTN64_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "7a13f0e41b30ea480a7ea9a7e22009909d9bf0cde91812a874089ffadf4908c6",
-    "fetch_kib": 45133.791, "fetch_scale": 524288 / 262166.4375,
-    "write_kib": 32963.557, "write_scale": 524288 / 524288.0,
+    "sha256": "f59f53c748eae457a76eb9c52015ad350c9d3d60f11e4c17b01b68d3193352d2",
+    "fetch_kib": 45286.380, "fetch_scale": 524288 / 262161.625,
+    "write_kib": 32920.951, "write_scale": 524288 / 524288.0,
 }
 
 
