@@ -11,14 +11,14 @@ ROOT = os.path.dirname(PKG)
 LIB_PATH = os.path.join(PKG, "libcsa2.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms stay off; fp16 packed math is unaffected
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
-    # works on them with VALU ops, so AGPR copies around every MFMA are avoided
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
+# matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
+# works on them with VALU ops, so AGPR copies around every MFMA are avoided
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def sources():
@@ -28,12 +28,30 @@ def sources():
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     out_tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", out_tmp]
+    obj_dir = os.path.join(PKG, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    # one object per source, compiled in parallel, then one link
+    procs, objs = [], []
+    for src in sources():
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *HIPCC_FLAGS, *VGPR_FORM, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    errors = []
+    for cmd, p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0:
+            errors.append(" ".join(cmd) + "\n" + out + err)
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     os.replace(out_tmp, LIB_PATH)
     return LIB_PATH
 

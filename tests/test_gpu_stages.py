@@ -514,9 +514,11 @@ def test_sparse_attn_global_fused_and_merge(csa2, H, split):
     (16, 200, 200, 128, True),    # 200 rows of 16 heads: one work-group per row
     (16, 300, 200, 128, False),   # 300 rows, an odd number of Top-K tiles per row
     (32, 130, 97, 100, True),     # 32 heads x 130 rows, split
+    (16, 1100, 512, 128, False),  # many rows (Top-512 + 128 SWA rows)
+    (32, 520, 97, 100, True),     # 32 heads x 520 rows, ragged
 ], ids=["h32_ragged_split", "h32_long_split", "h32_ragged", "h16_2048_1024_48splits", "h64_200rows",
         "h16_tiny_tiles", "h16_long_tiny_window", "h16_100rows", "h32_40rows", "h16_200rows", "h16_300rows",
-        "h32_130rows"])
+        "h32_130rows", "h16_1100rows", "h32_520rows"])
 def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
     rng = np.random.default_rng(k_pos + window)
     n_vis = max(3000, k_pos + 10)
