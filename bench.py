@@ -671,19 +671,18 @@ def pages_figures(c, step_ms_1m=None, step_ms_4k=None, launches=None):
     of the same 20-layer decode stack at 1M and at 4K context when given."""
     csa2, wl = c["csa2"], c["wl"]
     per_entry = c["cache"].nbytes // (c["B"] * c["T"])
-    split = csa2.csa2_attn_workspace_size(c["B"], c["H"], wl.k_pos, wl.swa) > 0
-    reuse = launches["reuse"]["kernels"] if launches else (2 if split else 1)
+    reuse = launches["reuse"]["kernels"] if launches else None
     return {
         "bytes_per_entry": {"csa2_amd": per_entry, "pages": 356},
         "bytes_per_token_at_2_5_entries": {"csa2_amd": per_entry * 2.5, "pages": 890},
         "kernels_per_reuse_layer_decode": {
             "csa2_amd": reuse,
             "pages": 11,
-            "note": "ours (counted in the step's graph when launches_per_layer is present): sparse "
-                    "attention with the SWA branch fused (+ the split merge at this batch); the pages "
-                    "count the whole fused layer"},
+            "note": "ours (counted in the step's graph): sparse attention with the SWA branch "
+                    "fused; up to 16 rows the split rows are merged inside the same kernel, from 17 "
+                    "rows on by a second one; the pages count the whole fused layer"},
         "kernels_per_reuse_layer_prefill": {
-            "csa2_amd": 1 if csa2.csa2_attn_workspace_size(4096, c["H"], wl.k_pos, wl.swa) == 0 else 2,
+            "csa2_amd": 1,
             "pages": 15,
             "note": "ours at the 4,096-query prefill chunk: one attention launch with the SWA branch fused"},
         "decode_flops_1m_over_4k": {

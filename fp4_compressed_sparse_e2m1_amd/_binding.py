@@ -316,9 +316,10 @@ def csa2_attn_workspace_size(n_rows: int, n_heads: int, k_pos: int, swa_window: 
 
 
 def attn_workspace(n_rows: int, n_heads: int, k_pos: int, swa_window: int, device="cuda"):
-    """Workspace for the split attention path, or None when no split is used."""
+    """Workspace for the split attention path (zero-filled, as its counters
+    must be before first use), or None when no split is used."""
     n = csa2_attn_workspace_size(n_rows, n_heads, k_pos, swa_window)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
 
 
 def _ws(workspace):

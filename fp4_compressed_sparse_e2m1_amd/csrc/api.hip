@@ -314,10 +314,14 @@ csa2_status attach_workspace(AttnArgs &a, int32_t n_rows, int32_t n_heads, int32
   const AttnPlan p = plan_attention(n_rows, n_heads, k_pos, window);
   a.n_split = 1;
   a.tiles_per_split = p.tiles_per_split;
-  if (!workspace || p.n_split <= 1) return CSA2_OK;
+  a.quarters = 0;
+  a.counters = nullptr;
+  if (!workspace || p.bytes == 0) return CSA2_OK;
   if (workspace_bytes < p.bytes || !aligned(workspace, kAlign)) return CSA2_E_WORKSPACE;
   a.n_split = p.n_split;
-  a.part_o = static_cast<float *>(workspace);
+  a.quarters = p.quarters;
+  a.counters = static_cast<uint32_t *>(workspace);
+  a.part_o = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kAttnCounterBytes);
   a.part_ml = a.part_o + (size_t)n_rows * p.n_split * n_heads * 512;
   return CSA2_OK;
 }
@@ -563,7 +567,15 @@ size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t k_pos,
   if (n_rows < 0 || (n_heads != 16 && n_heads != 32 && n_heads != 64) || k_pos < 0 ||
       k_pos > kMaxAttnPos || swa_window < 0 || swa_window > 1024)
     return 0;
-  return plan_attention(n_rows, n_heads, k_pos, swa_window).bytes;
+  // the most any call of 1 .. n_rows rows needs (the split, and so the
+  // bytes, are not monotonic in the row count; rows past 191 never split)
+  size_t most = 0;
+  const int32_t n = n_rows < 191 ? n_rows : 191;
+  for (int32_t r = 1; r <= n; ++r) {
+    const size_t b = plan_attention(r, n_heads, k_pos, swa_window).bytes;
+    most = b > most ? b : most;
+  }
+  return most;
 }
 
 const char *csa2_status_string(csa2_status status) {

@@ -10,6 +10,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -159,6 +160,14 @@ __device__ __forceinline__ float from_next_row(float x) {
   const int xi = __float_as_int(x);
   const auto sw = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
   return __int_as_float(sw[1]);
+}
+
+// Orders the LDS accesses of one wave before and after it (no work-group
+// barrier: the other waves are not involved).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));

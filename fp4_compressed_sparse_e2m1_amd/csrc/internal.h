@@ -99,12 +99,19 @@ struct AttnArgs {
   float *o;                   // [R][H][512]
   float *lse;                 // [R][H]
   int32_t merge_in;           // 1: start from (o, lse) as an earlier result
-  // split of a row's keys over several work-groups (n_split > 1):
-  // unnormalised partial results, merged by a second kernel
+  // split of a row's keys over several work-groups (n_split > 1), and for
+  // very few rows of 16 or 32 heads of its output channels (quarters):
+  // unnormalised partial results, merged by a second kernel or (quarters) by
+  // the last work-group to finish
   int32_t n_split;
-  int32_t tiles_per_split;    // key tiles (32 keys; 16-key blocks for 16 heads) per work-group
+  int32_t tiles_per_split;    // key tiles per work-group
+  int32_t quarters;           // 1: the quarter kernel (a workspace is attached)
   float *part_o;              // [R][n_split][H][512]
-  float *part_ml;             // [R][n_split][H][2]  (running max in log2 units, sum)
+  float *part_ml;             // [R][n_split][4][H][2] (quarters: one copy per channel
+                              // quarter) or [R][n_split][H][2]: running max in log2
+                              // units, sum
+  uint32_t *counters;         // quarters: [R][n_heads / 16][kAttnRowCounters] arrival
+                              // counters, zero between calls
   // set by launch_attention: all heads, head groups per row (a work-group
   // takes one group of 16 or 32 heads), rows
   int32_t n_heads;
@@ -115,12 +122,20 @@ struct AttnArgs {
 // Key tiles per attention work-group step.
 constexpr int kAttnTileKeys = 64;
 
-// Work-group split of the attention rows: n_split partial results per row
-// (1 = no split, no workspace).
+// The attention workspace starts with kAttnCounterBytes of arrival counters
+// (kAttnRowCounters per row and group of 16 heads: one per channel quarter,
+// one for the quarters' merges), then the partial results.
+constexpr int kAttnRowCounters = 8;
+constexpr size_t kAttnCounterBytes = 16384;
+
+// Work-group split of the attention rows: n_split partial results per row,
+// with quarters also four channel quarters (bytes = 0: no split, no
+// workspace).
 struct AttnPlan {
   int32_t n_split;
   int32_t tiles_per_split;
   size_t bytes;
+  int32_t quarters;
 };
 AttnPlan plan_attention(int32_t n_rows, int32_t n_heads, int32_t k_pos, int32_t window);
 

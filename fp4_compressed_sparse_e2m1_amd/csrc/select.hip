@@ -73,14 +73,6 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x + (row == 0 ? 0 : (row == 1 ? t0 : (row == 2 ? t0 + t1 : t0 + t1 + t2)));
 }
 
-// Orders the LDS accesses of one wave before and after it (no work-group
-// barrier: the other waves are not involved).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 struct Digit {
   int digit;   // bin holding the k_rem-th largest key
   int above;   // keys in higher bins

@@ -306,7 +306,12 @@ csa2_status csa2_index_reindex(const csa2_cache *cache, const uint16_t *q_idx, c
  * workspace (optional, 256-B aligned, csa2_attn_workspace_size bytes): with
  * it, a small batch spreads each row's keys over several work-groups and
  * merges their partial results; with workspace == NULL every row runs in one
- * work-group (same results up to fp32 rounding order, slower for few rows). */
+ * work-group (same results up to fp32 rounding order, slower for few rows).
+ * The workspace must be zero-filled before it is first passed to this
+ * function or to csa2_swa_merge: its first 16 KiB hold arrival counters,
+ * which every call that completes leaves at zero again (the rest is scratch),
+ * so one zero-filled workspace serves any number of calls.  Calls that share
+ * a workspace must not overlap in time (they would share the counters). */
 csa2_status csa2_sparse_attn(const csa2_cache *cache, const uint16_t *q, int32_t n_heads,
                              const int32_t *row_seq, int32_t n_rows, const int32_t *topk,
                              const int32_t *n_topk, int32_t k_pos, float scale,
@@ -329,9 +334,11 @@ csa2_status csa2_swa_merge(const uint16_t *q, int32_t n_heads, const int32_t *ro
                            void *stream);
 
 /* Scratch bytes that lets csa2_sparse_attn (k_pos, swa_window = the SWA
- * window or 0 without SWA) or csa2_swa_merge (k_pos = 0) split its rows over
- * several work-groups; 0 when no split is used for these sizes (a NULL
- * workspace is then fine).  Returns 0 for invalid arguments. */
+ * window or 0 without SWA) or csa2_swa_merge (k_pos = 0) split the rows of
+ * any call with 1 .. n_rows rows over several work-groups (the most any of
+ * those row counts needs); 0 when none of them splits (a NULL workspace is
+ * then fine).  Zero-fill it before its first use (see csa2_sparse_attn).
+ * Returns 0 for invalid arguments. */
 size_t csa2_attn_workspace_size(int32_t n_rows, int32_t n_heads, int32_t k_pos,
                                 int32_t swa_window);
 

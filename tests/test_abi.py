@@ -192,9 +192,14 @@ def test_attention_validation():
     # a split needs its workspace: given but too small is an error, NULL is not
     ws = lib.csa2_attn_workspace_size(8, 64, 512, 128)
     assert ws >= 8 * 2 * 64 * 514 * 4
-    assert lib.csa2_attn_workspace_size(8, 16, 512, 128) >= 8 * 10 * 16 * 514 * 4  # 20 tiles -> 10 parts
-    assert lib.csa2_attn_workspace_size(256, 16, 512, 128) == 0      # 16 heads, many rows: no split
-    assert lib.csa2_attn_workspace_size(256, 64, 512, 128) == 0      # many rows: no split
+    # counters, then the partials of several splits per row
+    assert lib.csa2_attn_workspace_size(8, 16, 512, 128) >= 16384 + 8 * 2 * 16 * 512 * 4
+    assert lib.csa2_attn_workspace_size(100, 16, 512, 128) > 0     # 16 heads, few rows: channel quarters
+    # sized for every call of up to n_rows rows (rows past 191 never split)
+    sizes = [lib.csa2_attn_workspace_size(n, 16, 512, 128) for n in range(1, 260)]
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+    assert sizes[255] == sizes[190] > 0
+    assert lib.csa2_attn_workspace_size(0, 16, 512, 128) == 0
     assert lib.csa2_attn_workspace_size(8, 24, 512, 128) == 0        # invalid heads
     a = list(base)
     a[2] = 64

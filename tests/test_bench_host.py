@@ -35,10 +35,12 @@ def test_pages_figures_from_the_cache_layout():
         nbytes = 8 * 1000 * (256 + 32 + 64 + 4)
 
     c = dict(csa2=csa2, wl=W.WORKLOADS[3], cache=Planes(), B=8, T=1000, H=16)
-    f = bench.pages_figures(c)
+    launches = {"full": {"kernels": 7}, "reindex": {"kernels": 3}, "reuse": {"kernels": 1}}
+    f = bench.pages_figures(c, launches=launches)
     assert f["bytes_per_entry"] == {"csa2_amd": 356, "pages": 356}
     assert f["bytes_per_token_at_2_5_entries"]["csa2_amd"] == 890
-    assert f["kernels_per_reuse_layer_decode"]["csa2_amd"] == 2     # attention + split merge at batch 8
+    assert f["kernels_per_reuse_layer_decode"]["csa2_amd"] == 1     # as counted in the step's graph
+    assert bench.pages_figures(c)["kernels_per_reuse_layer_decode"]["csa2_amd"] is None
     assert abs(f["decode_flops_1m_over_4k"]["csa2_amd"] - 2_734_686_208 / 469_762_048) < 1e-3
 
 

@@ -506,7 +506,7 @@ def test_sparse_attn_global_fused_and_merge(csa2, H, split):
     (32, 3, 1000, 100, True),     # the same with a long Top-K list
     (32, 3, 97, 100, False),
     (16, 1, 2048, 1024, True),    # 96 tiles over 48 work-groups: the merge's loop past 16 splits
-    (64, 200, 64, 32, True),      # 200 rows: no split even with a workspace requested
+    (64, 200, 64, 32, True),      # 200 rows: no split even with a workspace given
     (16, 5, 33, 1, True),         # one-row window, a 1-key second tile
     (16, 5, 1100, 1, True),       # a long Top-K list, a one-row window
     (16, 100, 512, 128, True),    # 100 rows: a few splits per row
@@ -532,7 +532,7 @@ def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
     assert c["topk"].shape[1] == k_pos
     ws = csa2.attn_workspace(n_rows, H, k_pos, window) if split else None
     if split:
-        assert (ws is None) == (n_rows >= 192)
+        assert ws is not None      # rows past 191 ignore it
     swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), window)
     o = torch.empty((n_rows, H, 512), device="cuda")
     lse = torch.empty((n_rows, H), device="cuda")
@@ -553,6 +553,45 @@ def test_sparse_attn_shapes(csa2, H, n_rows, k_pos, window, split):
     torch.cuda.synchronize()
     check_attention(o2.cpu().numpy(), lse2.cpu().numpy(), np.stack([x["o"] for x in refs]),
                     np.stack([x["lse"] for x in refs]), f"H{H} k{k_pos} w{window} merged")
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_attention_quarters_reuse_one_workspace(csa2, H):
+    """Very few rows split over key ranges and channel quarters count the
+    arrivals of their work-groups in the workspace's first 16 KiB, and every
+    call leaves those counters at zero: one zero-filled workspace then serves
+    calls of other row counts in turn, with and without the SWA merge (which
+    counts a second time for its lse)."""
+    rng = np.random.default_rng(41 + H)
+    n_max = 16 // (H // 16)
+    rows = [(np.sort(rng.choice(3000, int(rng.integers(1, 513)), replace=False)), 0) for _ in range(n_max)]
+    c = attn_case(csa2, H, [3000], rows, swa_ends=[200 - 7 * r for r in range(n_max)], seed=5 + H)
+    k_pos = c["topk"].shape[1]
+    ws = csa2.attn_workspace(n_max, H, k_pos, 128)
+    assert ws is not None
+    swa = csa2.Swa(dev(c["swa"]), dev(c["swa_end"]), c["window"])
+    refs = [oracle_attn(c, r) for r in range(n_max)]
+    for n in (n_max, 2, n_max - 1, 1):
+        assert csa2.csa2_attn_workspace_size(n, H, k_pos, 128) <= ws.numel()
+        sl = slice(0, n)
+        o = torch.empty((n, H, 512), device="cuda")
+        lse = torch.empty((n, H), device="cuda")
+        csa2.csa2_sparse_attn(c["cache"], dev(c["q"][sl]), dev(c["row_seq"][sl]), dev(c["topk"][sl]),
+                              dev(c["ntopk"][sl]), SCALE, o, lse, swa=swa, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.all(ws[:16384] == 0), f"counters left set after {n} rows"
+        check_attention(o.cpu().numpy(), lse.cpu().numpy(), np.stack([x["o"] for x in refs[:n]]),
+                        np.stack([x["lse"] for x in refs[:n]]), f"H{H} {n} rows")
+        # global keys first, then the SWA rows merged in, on the same workspace
+        o2 = torch.empty_like(o)
+        lse2 = torch.empty_like(lse)
+        csa2.csa2_sparse_attn(c["cache"], dev(c["q"][sl]), dev(c["row_seq"][sl]), dev(c["topk"][sl]),
+                              dev(c["ntopk"][sl]), SCALE, o2, lse2, workspace=ws)
+        csa2.csa2_swa_merge(dev(c["q"][sl]), dev(c["row_seq"][sl]), swa, SCALE, o2, lse2, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.all(ws[:16384] == 0), f"counters left set after the merge of {n} rows"
+        check_attention(o2.cpu().numpy(), lse2.cpu().numpy(), np.stack([x["o"] for x in refs[:n]]),
+                        np.stack([x["lse"] for x in refs[:n]]), f"H{H} {n} rows merged")
 
 
 @pytest.mark.parametrize("H", [16, 64])
