@@ -50,9 +50,9 @@ SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "2a0dfe19e124227aa6d4f3de514ede93d3c96a254524bf6c910fe07b85dc38b8",
-    "fetch_kib": 278659.698, "fetch_scale": 524288 / 262166.625,
-    "write_kib": 4096.484, "write_scale": 524288 / 524288.0,
+    "sha256": "92bd9b06b04388bf2aba08b65a605427bbda959f79f81dfdc111b2e703d8902c",
+    "fetch_kib": 278659.604, "fetch_scale": 524288 / 262165.875,
+    "write_kib": 4096.276, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -63,9 +63,9 @@ ATTN64_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "f59f53c748eae457a76eb9c52015ad350c9d3d60f11e4c17b01b68d3193352d2",
-    "fetch_kib": 45286.380, "fetch_scale": 524288 / 262161.625,
-    "write_kib": 32920.951, "write_scale": 524288 / 524288.0,
+    "sha256": "516758e24a55f9d55fcbd99f51d5cef766396b1b2f314f7f64efb8f28f6a59b7",
+    "fetch_kib": 45415.204, "fetch_scale": 524288 / 262161.8125,
+    "write_kib": 32921.777, "write_scale": 524288 / 524288.0,
 }
 
 
