@@ -213,6 +213,32 @@ def test_index_full_block_mode(csa2, case):
                        ntopk[r], ref, k_blk, k_pos, f"row {r}")
 
 
+def test_index_full_block_mode_tied_blocks(csa2):
+    """Four thousand blocks with one and the same top score, straddling the
+    boundary between the two first-level chunks of a 17,501-block row, around
+    the 2,048th place: the pool keeps the lowest-numbered tied blocks and the
+    Top-512 the lowest-numbered tied entries, exactly as the oracle ranks
+    (descending score, ties to the lower index) -- compared for equality, not
+    within the tie tolerance."""
+    n = 140001
+    base = W.rms_rows(n, 128, seed=81).numpy()
+    qidx = W.bf16_normal((1, 8, 128), seed=82)
+    w = W.uniform01((1, 8), seed=83)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    ikc0, iks0 = oracle.quantize(base, 32)
+    s0 = oracle.index_scores(qb[0], wn[0], ikc0, iks0, np.arange(n))
+    ik = base.copy()
+    ik[100000:132000] = 2.0 * base[int(np.argmax(s0))]     # blocks 12,500 .. 16,499, all tied
+    lat = W.rms_rows(n, 512, seed=84).numpy()
+    cache, ora = build_cache(csa2, [lat], [ik], n)
+    _, _, ikc, iks = ora[0]
+    pool, npool, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [0], [n], n, 2048, 512)
+    ref = oracle.full_layer_select(qb[0], wn[0], ikc, iks, n, 2048, 512)
+    assert list(ref["pool"][:3]) == [12500, 12501, 12502] and ref["pool"][-1] == 12500 + 2047
+    assert npool[0] == len(ref["pool"]) and np.array_equal(pool[0][:npool[0]], ref["pool"])
+    assert ntopk[0] == ref["n_topk"] == 512 and np.array_equal(topk[0], ref["topk"])
+
+
 @pytest.mark.parametrize("n_vis_rows", [[4096, 1000, 1], [20000, 16385, 300], [32768, 32767, 16385],
                                         [40000, 32769, 5], [140001, 70000]])
 def test_index_full_flat_mode(csa2, n_vis_rows):
