@@ -164,10 +164,12 @@ def csa2_workspace_size(op: int, n_rows: int, max_nvis: int, k_blocks: int, k_po
 
 
 def workspace(op: int, n_rows: int, max_nvis: int, k_blocks: int, k_pos: int, device="cuda"):
+    """Indexer workspace, zero-filled (its block-selection counters must be
+    zero before first use)."""
     n = csa2_workspace_size(op, n_rows, max_nvis, k_blocks, k_pos)
     if n == 0:
         raise ValueError("invalid workspace request")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def csa2_quantize_fp4(x, group, codes, scales, dst_rows=None, stream=None):

@@ -62,6 +62,7 @@ int32_t flat_pass_rows(int32_t n_rows, int32_t max_nvis, int32_t k_pos) {
 }
 
 struct Layout {
+  size_t counters = 0;  // arrival counters of the fused block selection (zero between calls)
   size_t keys_a = 0;    // block keys or flat entry keys
   size_t keys_b = 0;    // pool candidate keys
   size_t ping = 0, pong = 0;
@@ -76,6 +77,8 @@ Layout plan_workspace(int32_t op, int32_t rows, int32_t max_nvis, int32_t k_bloc
   size_t half = 0;
   if (k_blocks > 0) {
     if (op == CSA2_OP_INDEX_FULL || op == CSA2_OP_INDEX_POOL) {
+      L.counters = off;
+      off += round_up((size_t)rows * 4);
       const int64_t nb = ((int64_t)max_nvis + 7) / 8;
       if (op == CSA2_OP_INDEX_FULL) {
         L.keys_a = off;
@@ -112,12 +115,17 @@ struct SelectOut {
   int32_t k_blocks;
 };
 
+// counters (optional, [rows], zero between calls): two levels whose second
+// is one chunk then run as one launch.
 hipError_t run_select(const uint32_t *keys, int64_t stride, int count_kind, int count_fixed,
                       int64_t n_max, int k, const int32_t *row_seq, const int32_t *row_nvis,
                       int32_t n_seq, int32_t max_nvis, const SelectOut &fin, uint8_t *ping,
-                      uint8_t *pong, size_t half, int32_t rows, hipStream_t stream) {
+                      uint8_t *pong, size_t half, int32_t rows, hipStream_t stream,
+                      uint32_t *counters = nullptr) {
   int64_t chunks[8];
   const int levels = plan_levels(n_max, k, chunks);
+  const bool fused = counters && levels == 2 && chunks[0] * k <= kSelectChunk;
+  SelectArgs first = {};
   const uint32_t *kin = keys;
   const int32_t *iin = nullptr;
   int64_t in_stride = stride;
@@ -142,8 +150,12 @@ hipError_t run_select(const uint32_t *keys, int64_t stride, int count_kind, int 
       a.keys_out = reinterpret_cast<uint32_t *>(buf);
       a.ids_out = reinterpret_cast<int32_t *>(buf + half / 2);
       a.out_stride = out_stride;
-      hipError_t e = launch_select(a, rows, (int32_t)chunks[l], false, false, stream);
-      if (e != hipSuccess) return e;
+      if (fused) {
+        first = a;        // launched with the final level below
+      } else {
+        hipError_t e = launch_select(a, rows, (int32_t)chunks[l], false, false, stream);
+        if (e != hipSuccess) return e;
+      }
       kin = a.keys_out;
       iin = a.ids_out;
       in_stride = out_stride;
@@ -156,6 +168,11 @@ hipError_t run_select(const uint32_t *keys, int64_t stride, int count_kind, int 
       a.pool_blocks = fin.pool_blocks;
       a.n_pool = fin.n_pool;
       a.k_blocks = fin.k_blocks;
+      if (fused) {
+        hipError_t e = launch_select_levels(first, a, counters, rows, (int32_t)chunks[0], stream);
+        if (e != hipSuccess) return e;
+        continue;
+      }
       // a single level over more keys than one chunk: the wide selection
       const bool wide = levels == 1 && n_max > kSelectChunk;
       hipError_t e = launch_select(a, rows, 1, true, wide, stream);
@@ -282,7 +299,8 @@ csa2_status run_indexer(int32_t op, const csa2_cache *cache, const uint16_t *q_i
     }
     SelectOut fin = {pool_out, n_pool_out, kMapId, nullptr, nullptr, 0};
     e = run_select(bkeys, nb_stride, kCountNvisBlocks, 0, nb, k_blocks, row_seq, row_nvis,
-                   cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half, n_rows, stream);
+                   cache->n_seq, max_nvis, fin, ws + L.ping, ws + L.pong, L.half, n_rows, stream,
+                   reinterpret_cast<uint32_t *>(ws + L.counters));
     if (e != hipSuccess) return CSA2_E_HIP;
     pool = pool_out;
     npool = n_pool_out;

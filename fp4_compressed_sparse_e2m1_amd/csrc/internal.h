@@ -79,6 +79,12 @@ constexpr int kMaxPoolBlocks = 4096;
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
                          bool wide, hipStream_t stream);
+// Two levels of one launch: a1 the first level over n_chunks chunks per row
+// (its outputs in a1.keys_out / ids_out), a2 the final level over them; the
+// last chunk of each row to finish runs a2.  counters: [n_rows], zero between
+// calls.  Requires n_chunks * a1.k <= kSelectChunk.
+hipError_t launch_select_levels(const SelectArgs &a1, const SelectArgs &a2, uint32_t *counters,
+                                int32_t n_rows, int32_t n_chunks, hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

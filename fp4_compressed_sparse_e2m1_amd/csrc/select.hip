@@ -119,9 +119,13 @@ __device__ __forceinline__ Digit find_digit(const uint32_t *hist, int nb, int k_
 // KPT keys per thread: a work-group holds up to kSelThreads * KPT keys of a
 // row (16: the chunk of the multi-level selection; 32: a whole row of up to
 // 32,768 keys in one level).
-template <bool FINAL, bool IDS, int KPT = kKeysPerThread>
-__global__ void __launch_bounds__(kSelThreads)
-select_kernel(SelectArgs a) {
+// One selection work-group: row r, chunk `chunk` of its keys.  COH_IN reads
+// the keys and ids with device-scope loads and COH_OUT writes the level's
+// outputs with device-scope stores (both written through to / read from the
+// level every XCD sees): the two levels of select_levels_kernel hand their
+// data over inside one launch.
+template <bool FINAL, bool IDS, int KPT, bool COH_IN, bool COH_OUT>
+__device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk) {
   constexpr int kKeys = KPT;
   constexpr int kSpan = 64 * KPT;
   constexpr int kChunkKeys = kSelThreads * KPT;
@@ -135,8 +139,6 @@ select_kernel(SelectArgs a) {
   __shared__ uint32_t s_thr;
   __shared__ int s_keq;
 
-  const int r = blockIdx.y;
-  const int chunk = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -166,7 +168,10 @@ select_kernel(SelectArgs a) {
 #pragma unroll
   for (int j = 0; j < kKeys; ++j) {
     const int i = base + 64 * j;
-    key[j] = i < n_ld ? __builtin_nontemporal_load(&kin[i]) : 0u;   // read once
+    if constexpr (COH_IN)
+      key[j] = i < n_ld ? __hip_atomic_load(&kin[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    else
+      key[j] = i < n_ld ? __builtin_nontemporal_load(&kin[i]) : 0u;   // read once
   }
   int32_t ids[IDS ? kKeys : 1];
   if (IDS) {
@@ -174,7 +179,10 @@ select_kernel(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       const int i = base + 64 * j;
-      ids[j] = i < n_ld ? idin[i] : -1;
+      if constexpr (COH_IN)
+        ids[j] = i < n_ld ? __hip_atomic_load(&idin[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+      else
+        ids[j] = i < n_ld ? idin[i] : -1;
     }
   }
   // the pool row, for mapping candidate slots to entries (read in full;
@@ -225,6 +233,13 @@ select_kernel(SelectArgs a) {
   int32_t *out = FINAL ? a.out + (int64_t)r * a.k : nullptr;
   uint32_t *kout = FINAL ? nullptr : a.keys_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
   int32_t *iout = FINAL ? nullptr : a.ids_out + (int64_t)r * a.out_stride + (int64_t)chunk * a.k;
+  // a store of this level's intermediate output
+  auto put = [](auto *p, auto v) {
+    if constexpr (COH_OUT)
+      __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *p = v;
+  };
   // writes kept key k (carried id or chunk position `id`) to output slot pos
   auto emit = [&](int pos, uint32_t k, int id) {
     if (FINAL) {
@@ -235,8 +250,8 @@ select_kernel(SelectArgs a) {
       }
       out[pos] = id;
     } else {
-      kout[pos] = k;
-      iout[pos] = id;
+      put(kout + pos, k);
+      put(iout + pos, id);
     }
   };
 
@@ -525,13 +540,50 @@ select_kernel(SelectArgs a) {
     if (tid == 0) a.n_out[r] = k_eff;
   } else {
     for (int i = k_eff + tid; i < a.k; i += kSelThreads) {
-      kout[i] = 0u;
-      iout[i] = -1;
+      put(kout + i, 0u);
+      put(iout + i, -1);
     }
   }
 }
 
+template <bool FINAL, bool IDS, int KPT = kKeysPerThread>
+__global__ void __launch_bounds__(kSelThreads)
+select_kernel(SelectArgs a) {
+  select_run<FINAL, IDS, KPT, false, false>(a, blockIdx.y, blockIdx.x);
+}
+
+// Two levels in one launch: every work-group selects the Top-k of its chunk
+// (level 1, keys and ids written with device-scope stores) and counts its
+// arrival in counters[r]; the last of the row's chunks to arrive sets the
+// counter back to zero and runs the final level over the row's survivors
+// (device-scope loads).
+__global__ void __launch_bounds__(kSelThreads)
+select_levels_kernel(SelectArgs a1, SelectArgs a2, uint32_t *counters) {
+  __shared__ int s_last;
+  const int r = blockIdx.y;
+  select_run<false, false, kKeysPerThread, false, true>(a1, r, blockIdx.x);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counters + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == gridDim.x - 1;
+    if (last) __hip_atomic_store(counters + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  select_run<true, true, kKeysPerThread, true, false>(a2, r, 0);
+}
+
 }  // namespace
+
+hipError_t launch_select_levels(const SelectArgs &a1, const SelectArgs &a2, uint32_t *counters,
+                                int32_t n_rows, int32_t n_chunks, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  if (n_chunks < 1 || (int64_t)n_chunks * a1.k > kSelectChunk) return hipErrorInvalidValue;
+  select_levels_kernel<<<dim3((unsigned)n_chunks, (unsigned)n_rows), kSelThreads, 0, stream>>>(a1, a2, counters);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs &a, int32_t n_rows, int32_t n_chunks, bool final_level,
                          bool wide, hipStream_t stream) {

@@ -180,7 +180,12 @@ csa2_status csa2_cache_import(const csa2_cache *cache, int32_t seq, int64_t firs
  * (not valid for CSA2_OP_INDEX_POOL).  Flat mode scores and selects its rows
  * in passes of at most 256 MiB of scratch, so its size stays below that
  * bound (or one row's own need, 4 B per visible entry plus selection
- * scratch) however many rows a call has.  Returns 0 for invalid arguments. */
+ * scratch) however many rows a call has.  In block mode the workspace of
+ * csa2_index_full and csa2_index_pool begins with arrival counters (4 B per
+ * row) for a block selection that runs its two levels in one launch: zero-fill
+ * the workspace before its first use; every call that completes leaves the
+ * counters at zero again, so one workspace serves any number of calls (calls
+ * that share it must not overlap in time).  Returns 0 for invalid arguments. */
 size_t csa2_workspace_size(int32_t op, int32_t n_rows, int32_t max_nvis, int32_t k_blocks,
                            int32_t k_pos);
 
@@ -228,8 +233,10 @@ csa2_status csa2_index_full(const csa2_cache *cache, const uint16_t *q_idx, cons
  * held until the process ends; the current device's array is used (the
  * stream must belong to the current device), and its address is looked up
  * once per device on the first call there.  The call allocates nothing.
- * The array keeps the last call's contents; no call depends on them.  Calls
- * that overlap on one device (on different streams, or from different
+ * The array starts zeroed and keeps the last call's contents; a call relies
+ * only on the block selection's arrival counters being zero, which every
+ * completed call leaves them (see csa2_workspace_size).  Calls that overlap
+ * on one device (on different streams, or from different
  * threads before the earlier one's kernels finished) share the array and
  * race: order them on one stream.
  * Returns CSA2_E_UNSUPPORTED when these sizes need more scratch than the
