@@ -17,7 +17,7 @@ through four input sets (each layer's queries, indexer weights and SWA rows).
 
 The timed steps launch every kernel from Python (the GPU, not the host, is
 the limit: replaying the step as HIP graphs measured no faster); --graph
-replays it as three HIP graphs (the append, the scan, everything after it),
+replays it as two HIP graphs (the scan with its append, everything after it),
 after checking that a replay reproduces the eager step's outputs bit for bit.
 
 Output: one JSON line.  value = query tokens per second per CSA2 layer
@@ -41,6 +41,13 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 IK_BYTES = 68                  # indexer key bytes per entry (64 codes + 4 scales)
 BLOCK_KEY_BYTES = 4            # the scan writes one 4-B key per block of 8 entries
+APPEND_BYTES = 4 * (512 + 128) + 356   # per row: the fp32 latent and indexer key read, one entry written
+
+
+def scan_bytes_per_launch(T, B):
+    """Algorithmic HBM bytes of one scan-with-append launch: every visible
+    entry's indexer key once, plus each row's append."""
+    return IK_BYTES * T * B + APPEND_BYTES * B
 
 # HBM bytes per scan launch from two rocprofv3 counter runs of this bench
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same
@@ -48,11 +55,12 @@ BLOCK_KEY_BYTES = 4            # the scan writes one 4-B key per block of 8 entr
 # as built from these sources; once the sources differ the figure is dropped.
 SCAN_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/index.hip",
+                "fp4_compressed_sparse_e2m1_amd/csrc/encode.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "92bd9b06b04388bf2aba08b65a605427bbda959f79f81dfdc111b2e703d8902c",
-    "fetch_kib": 278659.604, "fetch_scale": 524288 / 262165.875,
-    "write_kib": 4096.276, "write_scale": 524288 / 524288.0,
+    "sha256": "5806cde2822378fe79fd25c60858aa567afaa7fa4120b704b2d0029100f96226",
+    "fetch_kib": 278742.177, "fetch_scale": 524288 / 262166.625,
+    "write_kib": 4099.052, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -63,9 +71,9 @@ ATTN64_COUNTERS = {
     "sources": ["fp4_compressed_sparse_e2m1_amd/csrc/attention64.hip",
                 "fp4_compressed_sparse_e2m1_amd/csrc/device.h",
                 "fp4_compressed_sparse_e2m1_amd/csrc/internal.h"],
-    "sha256": "516758e24a55f9d55fcbd99f51d5cef766396b1b2f314f7f64efb8f28f6a59b7",
-    "fetch_kib": 45415.204, "fetch_scale": 524288 / 262161.8125,
-    "write_kib": 32921.777, "write_scale": 524288 / 524288.0,
+    "sha256": "5adf8767c29c7dc4c1b8cbdaeeb42e3230534d38717e042d6bb430d64c02df9a",
+    "fetch_kib": 45558.027, "fetch_scale": 524288 / 262166.25,
+    "write_kib": 32924.391, "write_scale": 524288 / 524288.0,
 }
 
 
@@ -190,9 +198,11 @@ def _append(c):
     c["csa2"].csa2_cache_append(c["cache"], c["new_lat"], c["new_ik"], c["new_dst"])
 
 
-def _scan(c, l):
-    c["csa2"].csa2_index_scan(c["cache"], c["q_idx"][l], c["w"][l], c["row_seq"], c["row_nvis"], c["T"],
-                              c["block_keys"])
+def _scan_append(c, l):
+    """The Full layer's append of the step's new entry (at n_vis - 1 of each
+    sequence) and its scan, one launch."""
+    c["csa2"].csa2_index_scan_append(c["cache"], c["new_lat"], c["new_ik"], c["q_idx"][l], c["w"][l],
+                                     c["row_seq"], c["row_nvis"], c["T"], c["block_keys"])
 
 
 def _layer_tail(c, l, mode, src):
@@ -222,10 +232,9 @@ def step(c, ev=None):
     src = None
     for l, mode in enumerate(c["wl"].layers):
         if mode == "full":
-            _append(c)
             if ev is not None:
                 ev["scan0"].record()
-            _scan(c, l)
+            _scan_append(c, l)
             if ev is not None:
                 ev["scan1"].record()
         src = _layer_tail(c, l, mode, src)
@@ -234,7 +243,7 @@ def step(c, ev=None):
 
 
 def capture(c):
-    """The step as three HIP graphs: the append, the Full layer's scan, and
+    """The step as two HIP graphs: the Full layer's scan with its append, and
     everything after it (the stack opens with its one Full layer)."""
     import torch
 
@@ -247,7 +256,7 @@ def capture(c):
             src = _layer_tail(c, l, mode, src)
 
     graphs = []
-    for fn in (lambda: _append(c), lambda: _scan(c, 0), rest):
+    for fn in (lambda: _scan_append(c, 0), rest):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
@@ -258,7 +267,7 @@ def capture(c):
 
 def launches_per_layer(c):
     """Launches of each layer mode of the step, counted as the kernel nodes
-    of one HIP graph per layer (the Full layer's with its append and scan);
+    of one HIP graph per layer (the Full layer's with its scan-and-append);
     nodes of other kinds (copies, fills) are counted apart."""
     import ctypes
 
@@ -294,8 +303,7 @@ def launches_per_layer(c):
             continue
         if mode == "full":
             def fn(l=l):
-                _append(c)
-                _scan(c, l)
+                _scan_append(c, l)
                 _layer_tail(c, l, "full", None)
         else:
             def fn(l=l, mode=mode):
@@ -370,11 +378,10 @@ def run_gpu(c, steps, warmup, eager):
             step(c, dict(scan0=scan[k][0], scan1=scan[k][1], layer=[_NoEvent] * L))
         else:
             g = graphs[k % n_sets]
-            g[0].replay()
             scan[k][0].record()
-            g[1].replay()
+            g[0].replay()
             scan[k][1].record()
-            g[2].replay()
+            g[1].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     use_set(c, 0)
@@ -581,7 +588,7 @@ def decode_b32(steps, warmup):
     c = build(wid=2)
     wall, scan_ms, per_layer = run_gpu(c, steps, warmup, True)
     B, T, L = c["B"], c["T"], c["L"]
-    scan_bytes = IK_BYTES * T * B                  # key reads (68 B per visible entry)
+    scan_bytes = scan_bytes_per_launch(T, B)
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     modes = c["wl"].layers
     mode_us = {m: 1e3 * sum(t for t, mm in zip(per_layer, modes) if mm == m) /
@@ -864,7 +871,7 @@ def main():
     # algorithmic bytes of one scan launch: every entry's 68-B indexer key read
     # once (the 4-B block keys it writes per 8 entries are workspace traffic,
     # reported beside it, not counted)
-    scan_bytes = IK_BYTES * T * B
+    scan_bytes = scan_bytes_per_launch(T, B)
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     modes = c["wl"].layers
     mode_us = {m: 1e3 * sum(t for t, mm in zip(per_layer, modes) if mm == m) /
@@ -886,8 +893,8 @@ def main():
                    "layer_modes": {"full": 1, "reindex": 4, "reuse": 15}, "heads": c["H"],
                    "k_blocks": c["wl"].k_blk, "k_pos": c["wl"].k_pos, "swa": c["wl"].swa,
                    "parallelism": "single GPU",
-                   "launch": "HIP graph replay (append, scan, rest)" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "kernel": "score_kernel<block max> (csa2_index_scan)",
+                   "launch": "HIP graph replay (scan with append, rest)" if args.graph else "eager"},
+        "roofline": {"bound": "hbm", "kernel": "score_kernel<block max> (csa2_index_scan_append)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": scan_traffic_bytes(),
                      "algorithmic_bytes_per_launch": scan_bytes,
@@ -898,7 +905,7 @@ def main():
         "build_s": round(t_build, 1),
     }
     if not args.graph and not args.no_configs:
-        # the same step replayed as three HIP graphs (checked bit for bit
+        # the same step replayed as two HIP graphs (checked bit for bit
         # against the eager step first): the launch cost is the GPU's, not the host's
         wall_g, _, _ = run_gpu(c, args.steps, args.warmup, False)
         line["graph_replay_ms_per_step"] = round(wall_g * 1e3 / args.steps, 4)

@@ -70,6 +70,8 @@ def load():
         lib.csa2_index_full_noalloc.restype = ctypes.c_int
         lib.csa2_index_scan.argtypes = [P, P, P, P, P, i32, i32, P, P]
         lib.csa2_index_scan.restype = ctypes.c_int
+        lib.csa2_index_scan_append.argtypes = [P, P, P, P, P, P, P, i32, i32, P, P]
+        lib.csa2_index_scan_append.restype = ctypes.c_int
         lib.csa2_index_pool.argtypes = [P, P, P, P, P, i32, i32, P, i32, i32, P, P, P, P, P, sz, P]
         lib.csa2_index_pool.restype = ctypes.c_int
         lib.csa2_index_reindex.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, P, P, P, sz, P]
@@ -278,6 +280,21 @@ def csa2_index_scan(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, block_k
         _ptr(row_nvis, torch.int32, "row_nvis", (R,)), R, int(max_nvis),
         _ptr(block_keys, torch.int32, "block_keys", (R, max(1, (max_nvis + 7) // 8))), _stream(stream))
     _check("csa2_index_scan", st)
+
+
+def csa2_index_scan_append(cache: Cache, latent, ikey, q_idx, w, row_seq, row_nvis, max_nvis, block_keys,
+                           stream=None):
+    """Appends row r's latent [R, 512] / ikey [R, 128] at entry min(row_nvis[r], max_nvis) - 1 of
+    sequence row_seq[r] (rows name distinct sequences), then scans as csa2_index_scan, one launch."""
+    R = row_seq.shape[0]
+    cs = cache.struct()
+    st = load().csa2_index_scan_append(
+        ctypes.byref(cs), _ptr(latent, torch.float32, "latent", (R, 512)),
+        _ptr(ikey, torch.float32, "ikey", (R, 128)), _ptr(q_idx, torch.bfloat16, "q_idx", (R, 8, 128)),
+        _ptr(w, torch.float32, "w", (R, 8)), _ptr(row_seq, torch.int32, "row_seq", (R,)),
+        _ptr(row_nvis, torch.int32, "row_nvis", (R,)), R, int(max_nvis),
+        _ptr(block_keys, torch.int32, "block_keys", (R, max(1, (max_nvis + 7) // 8))), _stream(stream))
+    _check("csa2_index_scan_append", st)
 
 
 def csa2_index_pool(cache: Cache, q_idx, w, row_seq, row_nvis, max_nvis, block_keys, k_blocks, k_pos,

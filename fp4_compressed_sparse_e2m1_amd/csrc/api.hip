@@ -486,6 +486,30 @@ csa2_status csa2_index_scan(const csa2_cache *cache, const uint16_t *q_idx, cons
   return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
 }
 
+csa2_status csa2_index_scan_append(const csa2_cache *cache, const float *latent, const float *ikey,
+                                   const uint16_t *q_idx, const float *w, const int32_t *row_seq,
+                                   const int32_t *row_nvis, int32_t n_rows, int32_t max_nvis,
+                                   uint32_t *block_keys, void *stream) {
+  if (!cache_ok(cache, true, true)) return CSA2_E_INVALID_ARG;
+  const csa2_status cs = check_index_args(cache, q_idx, w, row_seq, row_nvis, n_rows, max_nvis);
+  if (cs != CSA2_OK) return cs;
+  if (!block_keys || !aligned(block_keys, 4)) return CSA2_E_INVALID_ARG;
+  if (!latent || !ikey || !aligned(latent, 16) || !aligned(ikey, 16)) return CSA2_E_INVALID_ARG;
+  if (n_rows > cache->n_seq) return CSA2_E_INVALID_ARG;   // rows name distinct sequences
+  ScoreArgs sa = score_args(cache, q_idx, w, row_seq, row_nvis, max_nvis);
+  const int64_t nb = ((int64_t)max_nvis + 7) / 8;
+  sa.keys_out = block_keys;
+  sa.out_stride = nb > 0 ? nb : 1;
+  sa.app_lat = latent;
+  sa.app_ik = ikey;
+  sa.kv_codes_w = cache->kv_codes;
+  sa.kv_scales_w = cache->kv_scales;
+  sa.ik_codes_w = cache->ik_codes;
+  sa.ik_scales_w = cache->ik_scales;
+  hipError_t e = launch_score(kScoreBlockMax, sa, n_rows, max_nvis, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA2_OK : CSA2_E_HIP;
+}
+
 csa2_status csa2_index_pool(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
                             const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
                             int32_t max_nvis, const uint32_t *block_keys, int32_t k_blocks,

@@ -26,6 +26,7 @@
 // The Top-K selection over the scores is in select.hip.
 
 #include "device.h"
+#include "encode.h"
 #include "internal.h"
 
 #include <type_traits>
@@ -51,8 +52,29 @@ __global__ void __launch_bounds__(kScoreThreads)
 score_kernel(ScoreArgs a) {
   constexpr int kChunk = CHUNK;
   constexpr int kTilesPerWave = kChunk / (4 * 16);
-  const int r = ROWFAST ? blockIdx.x : blockIdx.y;
-  const int chunk_id = ROWFAST ? blockIdx.y : blockIdx.x;
+  int r = ROWFAST ? blockIdx.x : blockIdx.y;
+  int chunk_id = ROWFAST ? blockIdx.y : blockIdx.x;
+  if (MODE == kScoreBlockMax && !ROWFAST && a.app_ik) {
+    // A scan with an append takes each row's chunks from the last (where a
+    // decode row's newest entry sits, encoded by that work-group before its
+    // scan), and the first work-groups dispatched, (x, 0) for x < n_rows,
+    // trade places with the rows' first ones, (0, x): every row's appending
+    // work-group starts at once and its longer run hides under the rest of
+    // the grid.  (Rows stay the slow index otherwise: interleaving the rows'
+    // chunks measured slower.)
+    const int x = blockIdx.x, y = blockIdx.y;
+    const int n_sw = (int)(gridDim.x < gridDim.y ? gridDim.x : gridDim.y);
+    if (y == 0 && x < n_sw) {
+      r = x;
+      chunk_id = (int)gridDim.x - 1;
+    } else if (x == 0 && y < n_sw) {
+      r = 0;
+      chunk_id = (int)gridDim.x - 1 - y;
+    } else {
+      r = y;
+      chunk_id = (int)gridDim.x - 1 - x;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int G = lane >> 4;
@@ -74,6 +96,25 @@ score_kernel(ScoreArgs a) {
   const int64_t n_slots = (MODE == kScorePool) ? (int64_t)8 * a.k_blocks : (int64_t)n_vis;
   const int64_t chunk0 = (int64_t)chunk_id * kChunk;
   if (chunk0 >= n_slots) return;
+
+  // A scan with an append: the work-group whose chunk holds the row's newest
+  // entry (n_vis - 1) first encodes it into both planes, as the append kernel
+  // would; the work-group barrier orders those stores before its own loads of
+  // the chunk (no other work-group reads the entry: one row per sequence).
+  if constexpr (MODE == kScoreBlockMax) {
+    const int64_t p = (int64_t)n_vis - 1;
+    if (a.app_ik && p >= chunk0 && p < chunk0 + kChunk) {
+      const int tid = threadIdx.x;
+      const int64_t prow = (int64_t)seq * a.cap + p;   // the entry's plane row
+      if (tid < 32)
+        encode_group<16>(a.app_lat + (int64_t)r * 512 + 16 * tid, a.kv_codes_w + prow * 256 + 8 * tid,
+                         a.kv_scales_w + prow * 32 + tid);
+      else if (tid < 36)
+        encode_group<32>(a.app_ik + (int64_t)r * 128 + 32 * (tid - 32), a.ik_codes_w + prow * 64 + 16 * (tid - 32),
+                         a.ik_scales_w + prow * 4 + (tid - 32));
+      __syncthreads();
+    }
+  }
 
   // Query operand: lane (G, c) holds head c's channels 32G + 8t .. +7, t = 0..3,
   // times the head's power of two 2^k (from its largest |q| over the four
@@ -418,7 +459,9 @@ hipError_t launch_score(ScoreMode mode, const ScoreArgs &a, int32_t n_rows, int6
   // Rows that share sequences (at least two rows per sequence on average)
   // share each key tile: the many-row kernel.  Rows of distinct sequences run
   // one per work-group.
-  if (mode != kScorePool && n_rows >= kScoreRowsMin && n_rows >= 2 * (int64_t)a.n_seq &&
+  // (A scan with an append keeps one row per work-group: its rows name
+  // distinct sequences.)
+  if (mode != kScorePool && !a.app_ik && n_rows >= kScoreRowsMin && n_rows >= 2 * (int64_t)a.n_seq &&
       slots <= ((int64_t)1 << 30)) {
     // 8 rows per work-group; 4 when the sequences have at most 4 rows each on
     // average (a few queries per sequence), so a work-group's rows are mostly

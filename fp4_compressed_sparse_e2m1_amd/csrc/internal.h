@@ -33,6 +33,11 @@ struct ScoreArgs {
   int32_t k_blocks;
   uint32_t *keys_out;         // [R][out_stride] order-preserving score keys
   int64_t out_stride;
+  // block-max scan that first appends each row's newest entry (entry
+  // n_vis - 1 of its sequence) to both planes (null: no append)
+  const float *app_lat;       // [R][512]
+  const float *app_ik;        // [R][128]
+  uint8_t *kv_codes_w, *kv_scales_w, *ik_codes_w, *ik_scales_w;
 };
 
 // Entries per work-group of the scoring kernel (scan / flat, and pool mode).

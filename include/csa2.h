@@ -17,7 +17,9 @@
  * A layer in each mode is a sequence of calls:
  *   Full    = csa2_cache_append (its new entries, both planes; or
  *             csa2_quantize_fp4 per plane)
- *             + csa2_index_full + csa2_sparse_attn [+ csa2_swa_merge]
+ *             + csa2_index_full + csa2_sparse_attn [+ csa2_swa_merge];
+ *             or, one new entry per sequence, csa2_index_scan_append +
+ *             csa2_index_pool + csa2_sparse_attn [+ csa2_swa_merge]
  *   Reindex = csa2_index_reindex (on the Full layer's cache and pool)
  *             + csa2_sparse_attn [+ csa2_swa_merge]
  *   Reuse   = csa2_sparse_attn [+ csa2_swa_merge] on the inherited Top-K.
@@ -263,6 +265,27 @@ csa2_status csa2_index_full_noalloc(const csa2_cache *cache, const uint16_t *q_i
 csa2_status csa2_index_scan(const csa2_cache *cache, const uint16_t *q_idx, const float *w,
                             const int32_t *row_seq, const int32_t *row_nvis, int32_t n_rows,
                             int32_t max_nvis, uint32_t *block_keys, void *stream);
+
+/* S1 + S2 in one launch -- a decode step's append of each row's new entry
+ * followed by the block-mode scan of csa2_index_scan [P3 "레이어 40개 가운데
+ * 4개만...": each Full layer stores the step's new entry in both planes and
+ * then scores every visible entry, the new one included].  For each row r
+ * with 0 <= row_seq[r] < n_seq and n = min(row_nvis[r], max_nvis) >= 1,
+ * latent row r (fp32 [n_rows][512]) and indexer-key row r (fp32
+ * [n_rows][128]) are encoded into plane row row_seq[r] * cap + n - 1 with the
+ * bytes csa2_cache_append writes there; then block_keys is written exactly as
+ * csa2_index_scan writes it on the updated cache.  Other rows append nothing.
+ * Precondition: the rows name distinct sequences (one new entry per
+ * sequence, as in a decode step); rows sharing a sequence give unspecified
+ * plane bytes and keys for it (every access stays inside the planes).  A
+ * launch reads no entry another row writes, so no ordering beyond the stream
+ * is needed.  latent and ikey must be 16-B aligned; the cache needs all four
+ * planes; n_rows > n_seq is rejected (CSA2_E_INVALID_ARG), other rules as
+ * csa2_index_scan. */
+csa2_status csa2_index_scan_append(const csa2_cache *cache, const float *latent, const float *ikey,
+                                   const uint16_t *q_idx, const float *w, const int32_t *row_seq,
+                                   const int32_t *row_nvis, int32_t n_rows, int32_t max_nvis,
+                                   uint32_t *block_keys, void *stream);
 
 /* S3 + S4 on a finished scan -- the remaining stages of csa2_index_full in
  * block mode: block Top-k_blocks from block_keys (as written by

@@ -28,7 +28,7 @@ def test_exports_every_declared_function():
     lib = csa2.load()
     names = declared_functions()
     assert {"csa2_quantize_fp4", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
-            "csa2_swa_merge", "csa2_index_scan", "csa2_index_pool"} <= set(names)
+            "csa2_swa_merge", "csa2_index_scan", "csa2_index_scan_append", "csa2_index_pool"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in csa2.h but not exported"
 
@@ -141,6 +141,21 @@ def test_index_validation():
     scan = lib.csa2_index_scan
     assert scan(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, None, None) == INVALID
     assert scan(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 101, FAKE, None) == INVALID
+    sa = lib.csa2_index_scan_append
+    c4 = cache_struct(n_seq=4)
+
+    def sa_call(cache=None, lat=FAKE, ik=FAKE, R=2, max_nvis=100, keys=FAKE):
+        return sa(ctypes.byref(cache if cache is not None else c4), lat, ik, FAKE, FAKE, FAKE, FAKE, R,
+                  max_nvis, keys, None)
+
+    assert sa_call(R=5) == INVALID                        # more rows than sequences
+    assert sa_call(cache=c, R=2) == INVALID               # (c holds one sequence)
+    assert sa_call(keys=None) == INVALID
+    assert sa_call(lat=None) == INVALID
+    assert sa_call(ik=FAKE + 4) == INVALID                # misaligned indexer keys
+    assert sa_call(max_nvis=101) == INVALID               # beyond cap
+    assert sa_call(R=0) == INVALID
+    assert sa_call(cache=B._CacheStruct(0, 0, FAKE, FAKE, 100, 4)) == INVALID   # no latent planes
     pool = lib.csa2_index_pool
     assert pool(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 2, 100, FAKE, 0, 16, FAKE, FAKE, FAKE,
                 FAKE, FAKE, 1 << 30, None) == INVALID     # pool stage needs k_blocks >= 1

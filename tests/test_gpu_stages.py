@@ -125,6 +125,52 @@ def test_cache_append_both_planes(csa2):
         assert not got[untouched].any()
 
 
+def test_index_scan_append_matches_append_then_scan(csa2):
+    """The one-launch append + scan writes the planes and block keys that the
+    append at entry min(n_vis, max_nvis) - 1 followed by the scan write, byte
+    for byte, and the appended bytes are the oracle's encoding.  The new
+    entries sit at the start, the middle and the end of a 512-entry scan
+    chunk, at entry 0, and past max_nvis (clamped); rows with n_vis 0 or an
+    invalid sequence append nothing."""
+    n_seq, cap, max_nvis = 8, 2600, 2500
+    seqs = np.array([3, 0, 7, 1, 4, -1, 6, 2], np.int32)
+    nvis = np.array([513, 1024, 1, 2100, 0, 300, 2599, 777], np.int32)
+    R = len(seqs)
+    g = torch.Generator(device="cpu").manual_seed(12)
+    planes = [torch.randint(0, 256, (n_seq, cap, 256), generator=g, dtype=torch.uint8),
+              torch.randint(0, 0x7F, (n_seq, cap, 32), generator=g, dtype=torch.uint8),
+              torch.randint(0, 256, (n_seq, cap, 64), generator=g, dtype=torch.uint8),
+              torch.randint(0, 0x7F, (n_seq, cap, 4), generator=g, dtype=torch.uint8)]
+    ca = csa2.Cache(n_seq, cap, planes=[p.cuda() for p in planes])
+    cb = csa2.Cache(n_seq, cap, planes=[p.cuda() for p in planes])
+    lat = W.rms_rows(R, 512, seed=91).numpy()
+    ik = W.rms_rows(R, 128, seed=92).numpy()
+    lat[2] *= 3e-5                                  # subnormal scales
+    ik[3] *= 60.0                                   # saturating scales
+    q_idx = W.bf16_normal((R, 8, 128), 93, device="cuda")
+    w = W.uniform01((R, 8), 94, device="cuda")
+    n_eff = np.minimum(nvis, max_nvis)
+    ok = (seqs >= 0) & (seqs < n_seq) & (n_eff >= 1)
+    dst = np.where(ok, seqs.astype(np.int64) * cap + n_eff - 1, -1)
+    ka = csa2.block_keys_buffer(R, max_nvis).fill_(0x5A5A5A5A)
+    kb = csa2.block_keys_buffer(R, max_nvis).fill_(0x5A5A5A5A)
+    csa2.csa2_cache_append(ca, dev(lat), dev(ik), dev(dst))
+    csa2.csa2_index_scan(ca, q_idx, w, dev(seqs), dev(nvis), max_nvis, ka)
+    csa2.csa2_index_scan_append(cb, dev(lat), dev(ik), q_idx, w, dev(seqs), dev(nvis), max_nvis, kb)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kb.cpu().numpy(), ka.cpu().numpy())
+    kvc, kvs = oracle.quantize(lat, 16)
+    ikc, iks = oracle.quantize(ik, 32)
+    for a, b, ref in ((ca.kv_codes, cb.kv_codes, kvc), (ca.kv_scales, cb.kv_scales, kvs),
+                      (ca.ik_codes, cb.ik_codes, ikc), (ca.ik_scales, cb.ik_scales, iks)):
+        bh = b.reshape(n_seq * cap, -1).cpu().numpy()
+        np.testing.assert_array_equal(bh, a.reshape(n_seq * cap, -1).cpu().numpy())
+        np.testing.assert_array_equal(bh[dst[ok]], ref[ok])
+    # an n_vis-0 row and an invalid sequence left their planes alone
+    for p_ref, b in zip(planes, (cb.kv_codes, cb.kv_scales, cb.ik_codes, cb.ik_scales)):
+        assert torch.equal(b[4].cpu(), p_ref[4]) and torch.equal(b[5].cpu(), p_ref[5])
+
+
 def test_cache_records_export_import(csa2):
     """Entry records (356 B: kv codes, kv scales, indexer codes, indexer
     scales) equal the oracle's encoding of the same rows laid out in that
