@@ -80,6 +80,12 @@ struct Digit {
   int total;   // keys in the whole histogram
 };
 
+// Sum of s[v] over the waves v below `wave` (lane v reads s[v]).
+__device__ __forceinline__ int sum_below(const int *s, int wave, int lane) {
+  const int x = lane < wave ? s[lane] : 0;
+  return (int)wave_reduce((uint32_t)x, lane, [](uint32_t p, uint32_t q) { return p + q; });
+}
+
 // One wave finds, in a histogram of nb bins (a power of two, 2 .. 4096), the
 // bin that holds the k_rem-th largest key, counting from the top bin down.
 // Lane l first sums the l-th group of nb/64 bins from the top; a prefix sum
@@ -90,7 +96,20 @@ __device__ __forceinline__ Digit find_digit(const uint32_t *hist, int nb, int k_
   const int top = nb - lane * per;        // this lane's group: bins [top - per, top)
   int local = 0;
   if (top > 0) {
-    if (per >= 4) {
+    if (per == 64) {
+      // 4,096 bins: sixteen 16-B reads per lane, eight in flight at once; lane l
+      // starts its group at read l mod 16, so that the lanes' reads (256 B
+      // apart) fall on different banks
+#pragma unroll
+      for (int h = 0; h < 16; h += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          v[i] = *reinterpret_cast<const uint4 *>(&hist[top - 64 + 4 * ((h + i + lane) & 15)]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) local += (int)(v[i].x + v[i].y + v[i].z + v[i].w);
+      }
+    } else if (per >= 4) {
       for (int i = 0; i < per; i += 4) {
         const uint4 v = *reinterpret_cast<const uint4 *>(&hist[top - per + i]);
         local += (int)(v.x + v.y + v.z + v.w);
@@ -303,8 +322,7 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
       for (int j = 0; j < kKeys; ++j) cnt += __popcll(__ballot(key[j] != 0u && key[j] >= lo_key));
       if (lane == 0) s_red[wave] = cnt;
       __syncthreads();
-      int off = 0;
-      for (int v = 0; v < wave; ++v) off += s_red[v];
+      int off = sum_below(s_red, wave, lane);
 #pragma unroll
       for (int j = 0; j < kKeys; ++j) {
         const bool m = key[j] != 0u && key[j] >= lo_key;
@@ -376,8 +394,7 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
       const int incl = wave_incl_scan(packed, lane);
       if (lane == 63) s_red[wave] = incl;
       __syncthreads();
-      int run = incl - packed;
-      for (int v = 0; v < wave; ++v) run += s_red[v];
+      int run = incl - packed + sum_below(s_red, wave, lane);
       int run_gt = run & 0xFFFF, run_eq = run >> 16;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -448,8 +465,7 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
               cnt += __popcll(__ballot(key[j] != 0u && (key[j] & mask) == prefix));
             if (lane == 0) s_red[wave] = cnt;
             __syncthreads();
-            int off = 0;
-            for (int v = 0; v < wave; ++v) off += s_red[v];
+            int off = sum_below(s_red, wave, lane);
   #pragma unroll
             for (int j = 0; j < kKeys; ++j) {
               const bool m = key[j] != 0u && (key[j] & mask) == prefix;
@@ -514,11 +530,8 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
       s_red[kSelWaves + wave] = (int)ceq;
     }
     __syncthreads();
-    int run_gt = 0, run_eq = 0;
-    for (int v = 0; v < wave; ++v) {
-      run_gt += s_red[v];
-      run_eq += s_red[kSelWaves + v];
-    }
+    int run_gt = sum_below(s_red, wave, lane);
+    int run_eq = sum_below(s_red + kSelWaves, wave, lane);
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
   #pragma unroll
     for (int j = 0; j < kKeys; ++j) {
