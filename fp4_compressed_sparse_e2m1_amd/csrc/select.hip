@@ -157,6 +157,8 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
   __shared__ int s_digit, s_above, s_ncand, s_flag;
   __shared__ uint32_t s_thr;
   __shared__ int s_keq;
+  __shared__ uint32_t s_bin[64];   // the boundary bin's keys, when it holds at most 64
+  __shared__ int s_nbin;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -314,6 +316,7 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
     if (listed) {
       // bins 0 .. 191 serve the two refining passes below
       if (tid < 192) hist[tid] = 0;
+      if (tid == 0) s_nbin = 0;
       const uint32_t lo_key = (base_bin + (uint32_t)s_digit) << shift0;
       const int n_list = s_above + s_ncand;
       const unsigned long long lt = (1ull << lane) - 1ull;
@@ -346,46 +349,81 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
         lk[q] = e < n_list ? s_lkey[e] : 0u;
         li[q] = e < n_list ? s_lid[e] : -1;
       }
-      const int wA = shift0 < 7 ? shift0 : 7;
-      const int sA = shift0 - wA;
-      uint32_t prefix = lo_key;
-      int k_rem = k_eff - s_above;
-      if (wA > 0) {
+      uint32_t thr;
+      int k_eq;
+      const int n_bin = s_ncand;   // the boundary bin's keys, all in the list
+      if (n_bin >= 1 && n_bin <= 64) {
+        // Few keys share the boundary bin: rank them directly.  Every thread
+        // adds its list entries of that bin to s_bin (in any order: only their
+        // values matter), and wave 0 takes the (k_eff - s_above)-th largest of
+        // them by counting, for each, the bin's keys above it and at least it.
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (lk[q] != 0u && (lk[q] >> shift0) == (prefix >> shift0))
-            atomicAdd(&hist[(lk[q] >> sA) & ((1u << wA) - 1u)], 1u);
+          if (lk[q] != 0u && (lk[q] >> shift0) == (lo_key >> shift0)) s_bin[atomicAdd(&s_nbin, 1)] = lk[q];
         __syncthreads();
         if (wave == 0) {
-          const Digit d = find_digit(hist, 1 << wA, k_rem, lane);
+          const int k_rem = k_eff - s_above;
+          const uint32_t v = lane < n_bin ? s_bin[lane] : 0u;
+          int gt = 0, ge = 0;
+          for (int i = 0; i < n_bin; ++i) {
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, i);
+            gt += o > v;
+            ge += o >= v;
+          }
+          const unsigned long long hit = __ballot(lane < n_bin && gt < k_rem && ge >= k_rem);
+          const int l = hit ? __ffsll((long long)hit) - 1 : 0;
+          const uint32_t tv = (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+          const int tg = __builtin_amdgcn_readlane(gt, l);
           if (lane == 0) {
-            s_digit = d.digit;
-            s_above = d.above;
+            s_thr = tv;
+            s_keq = k_rem - tg;
           }
         }
         __syncthreads();
-        prefix |= (uint32_t)s_digit << sA;
-        k_rem -= s_above;
-      }
-      if (sA > 0) {
+        thr = s_thr;
+        k_eq = s_keq;
+      } else {
+        const int wA = shift0 < 7 ? shift0 : 7;
+        const int sA = shift0 - wA;
+        uint32_t prefix = lo_key;
+        int k_rem = k_eff - s_above;
+        if (wA > 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (lk[q] != 0u && (lk[q] >> sA) == (prefix >> sA)) atomicAdd(&hist[128 + (lk[q] & ((1u << sA) - 1u))], 1u);
-        __syncthreads();
-        if (wave == 0) {
-          const Digit d = find_digit(hist + 128, 1 << sA, k_rem, lane);
-          if (lane == 0) {
-            s_digit = d.digit;
-            s_above = d.above;
+          for (int q = 0; q < 4; ++q)
+            if (lk[q] != 0u && (lk[q] >> shift0) == (prefix >> shift0))
+              atomicAdd(&hist[(lk[q] >> sA) & ((1u << wA) - 1u)], 1u);
+          __syncthreads();
+          if (wave == 0) {
+            const Digit d = find_digit(hist, 1 << wA, k_rem, lane);
+            if (lane == 0) {
+              s_digit = d.digit;
+              s_above = d.above;
+            }
           }
+          __syncthreads();
+          prefix |= (uint32_t)s_digit << sA;
+          k_rem -= s_above;
         }
-        __syncthreads();
-        prefix |= (uint32_t)s_digit;
-        k_rem -= s_above;
+        if (sA > 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (lk[q] != 0u && (lk[q] >> sA) == (prefix >> sA)) atomicAdd(&hist[128 + (lk[q] & ((1u << sA) - 1u))], 1u);
+          __syncthreads();
+          if (wave == 0) {
+            const Digit d = find_digit(hist + 128, 1 << sA, k_rem, lane);
+            if (lane == 0) {
+              s_digit = d.digit;
+              s_above = d.above;
+            }
+          }
+          __syncthreads();
+          prefix |= (uint32_t)s_digit;
+          k_rem -= s_above;
+        }
+        // every thread has followed the same digits
+        thr = prefix;
+        k_eq = k_rem;
       }
-      // every thread has followed the same digits
-      const uint32_t thr = prefix;
-      const int k_eq = k_rem;
       // ordered compaction of the list; above-threshold and tie counts
       // travel packed in one prefix sum
       int packed = 0;
@@ -435,7 +473,7 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
           const int width = top + 1 < kSelBits ? top + 1 : kSelBits;
           const int shift = top + 1 - width;
           const uint32_t dmask = (1u << width) - 1u;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < kKeys; ++j)
             if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
           __syncthreads();
@@ -453,20 +491,20 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
           k_rem -= s_above;
           const int ncand = s_ncand;
           top = shift - 1;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < kSelBins / kSelThreads; ++i) hist[tid + kSelThreads * i] = 0;
           if (top >= 0 && ncand <= kCandCap) {
             // gather the keys still in play, wave by wave (per-wave counts,
             // then each wave's offset)
             const unsigned long long lt = (1ull << lane) - 1ull;
             int cnt = 0;
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < kKeys; ++j)
               cnt += __popcll(__ballot(key[j] != 0u && (key[j] & mask) == prefix));
             if (lane == 0) s_red[wave] = cnt;
             __syncthreads();
             int off = sum_below(s_red, wave, lane);
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < kKeys; ++j) {
               const bool m = key[j] != 0u && (key[j] & mask) == prefix;
               const unsigned long long bm = __ballot(m);
@@ -518,7 +556,7 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
     // above the threshold before it) + min(#threshold ties before it, k_eq),
     // counted with ballots; ties are taken lowest position first.
     uint32_t cgt = 0, ceq = 0;
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       cgt += key[j] > thr;
       ceq += (key[j] == thr) && (base + 64 * j < n);
@@ -533,7 +571,7 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
     int run_gt = sum_below(s_red, wave, lane);
     int run_eq = sum_below(s_red + kSelWaves, wave, lane);
     const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < kKeys; ++j) {
       const int i = base + 64 * j;
       const uint32_t k = key[j];
