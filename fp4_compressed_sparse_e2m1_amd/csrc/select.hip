@@ -7,9 +7,11 @@
 // first digit -- a window ending at the largest key, or the plain digit below
 // the highest bit in which the keys differ -- names the bin holding the k-th
 // key; the keys at or above that bin are gathered, in position order with
-// their ids, into an LDS list; the remaining bits are resolved from the list
-// and the output is compacted from it, ties at the threshold going to the
-// lowest positions.  A generic radix path (12-bit digits, then one wave on the
+// their ids, into an LDS list; the threshold inside that bin is found by
+// ranking the bin's keys directly when it holds at most 64, else by resolving
+// the remaining bits from the list with two more digits, and the output is
+// compacted from the list, ties at the threshold going to the lowest
+// positions.  A generic radix path (12-bit digits, then one wave on the
 // keys still in play, then a ballot-ordered compaction from registers) covers
 // the cases the list cannot hold.  Rows with more keys are cut into chunks
 // whose Top-k survivors feed a further level, which keeps the result exact
@@ -282,8 +284,9 @@ __device__ __forceinline__ void select_run(const SelectArgs &a, int r, int chunk
   // finely), or the plain digit of up to 12 bits below the highest bit in
   // which the keys differ.  Its histogram names the bin that holds the
   // k_eff-th largest key; every key at or above that bin goes, in position
-  // order, into an LDS list (about k_eff keys plus one bin); the remaining
-  // (at most 13) bits are resolved block-wide from the list, and the output
+  // order, into an LDS list (about k_eff keys plus one bin); the threshold
+  // inside the bin comes from ranking its keys (at most 64 of them) or from
+  // the remaining (at most 13) bits resolved block-wide from the list, and the output
   // is compacted from the list.  Falls back to the generic path when the
   // k_eff-th key lies below the window or the list would overflow.
   bool listed = false;
