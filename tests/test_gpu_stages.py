@@ -285,6 +285,39 @@ def test_index_full_block_mode_tied_blocks(csa2):
     assert ntopk[0] == ref["n_topk"] == 512 and np.array_equal(topk[0], ref["topk"])
 
 
+@pytest.mark.parametrize("n_tied", [40, 70])
+def test_index_flat_tied_threshold(csa2, n_tied):
+    """n_tied entries with one and the same score straddle the 512th place of
+    a 10,000-entry flat selection: 40 leave the threshold's bin small enough to
+    be ranked directly, 70 send it through the refining digits.  The Top-512
+    must take exactly the lowest-numbered tied entries the oracle takes."""
+    n, k = 10000, 512
+    base = W.rms_rows(n, 128, seed=91).numpy()
+    qidx = W.bf16_normal((1, 8, 128), seed=92)
+    w = W.uniform01((1, 8), seed=93)
+    qb, wn = W.bf16_bits(qidx), w.numpy()
+    slots = np.arange(1000, 1000 + 97 * n_tied, 97)[:n_tied]      # spread over the row
+    c0, s0 = oracle.quantize(base, 32)
+    order = np.argsort(-oracle.index_scores(qb[0], wn[0], c0, s0, np.arange(n)), kind="stable")
+    for rank in range(480, 520):        # copy the rank-th entry's key into the slots
+        ik = base.copy()
+        ik[slots] = base[int(order[rank])]
+        c1, s1 = oracle.quantize(ik, 32)
+        sc = oracle.index_scores(qb[0], wn[0], c1, s1, np.arange(n))
+        above = int((sc > sc[slots[0]]).sum())
+        if above < k <= above + n_tied and above + n_tied - k >= 4 and k - above >= 4:
+            break
+    assert above < k <= above + n_tied, "no straddling tie found"
+    lat = W.rms_rows(n, 512, seed=94).numpy()
+    cache, ora = build_cache(csa2, [lat], [ik], n)
+    _, _, ikc, iks = ora[0]
+    _, _, topk, ntopk = run_full(csa2, cache, dev(qidx), dev(w), [0], [n], n, 0, k)
+    ref = oracle.full_layer_select(qb[0], wn[0], ikc, iks, n, 0, k)
+    assert ntopk[0] == ref["n_topk"] == k and np.array_equal(topk[0], ref["topk"])
+    kept = np.intersect1d(topk[0], slots)
+    assert len(kept) == k - above and np.array_equal(kept, slots[:k - above])
+
+
 @pytest.mark.parametrize("n_vis_rows", [[4096, 1000, 1], [20000, 16385, 300], [32768, 32767, 16385],
                                         [40000, 32769, 5], [140001, 70000]])
 def test_index_full_flat_mode(csa2, n_vis_rows):
